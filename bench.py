@@ -1,0 +1,243 @@
+"""Benchmark of the MoE expert layer on one MI355X.
+
+A step is one pass of the whole layer path (route -> align -> expert FFN with
+combine) over every layer of the workload, on one stream (captured as a HIP
+graph unless --eager). Inputs are synthetic (gen/) and resident in HBM before
+the timed region. Prints one JSON line.
+
+Default workload: the decode-regime layer stack -- T=32 tokens through 40
+layers of H=2048, I=512, E=256, top-8, each with its own 102-slot FP8 pool
+(grown to hold every routed expert when more are needed).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="C1")
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per layer (default: largest decode T)")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--act", choices=["auto", "bf16", "fp8"], default="auto")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "moe_expert_layer_topk_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer runs unsharded on one MI355X); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_expert_layer_topk_amd as moe
+    from gen import CONFIGS, make_layer, make_bank
+    from harness import device_pool, device_inputs, bank_on_device, oracle_layer
+
+    cfg = CONFIGS[args.config]
+    T = args.tokens or (max(t for t in cfg.Ts if t <= 64) if min(cfg.Ts) <= 64 else cfg.Ts[0])
+    L = args.layers or cfg.layers
+    act = {"bf16": moe.ACT_BF16, "fp8": moe.ACT_FP8_G128_POW2}.get(args.act)
+    if act is None:
+        act = moe.ACT_BF16 if T <= 64 else moe.ACT_FP8_G128_POW2
+    bm = args.block_m or (16 if act == moe.ACT_BF16 else 128)
+    dev = torch.device("cuda:0")
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+
+    t0 = time.time()
+    bank = make_bank(cfg)
+    bdev = bank_on_device(bank, dev)
+    layers = []
+    for l in range(L):
+        li = make_layer(cfg, T, l)
+        pool = device_pool(li, bank, dev, bdev)
+        x, logits, soe, mask = device_inputs(li, dev)
+        cap = moe.align_capacity(T, k, E, bm)
+        buf = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   err=torch.zeros(1, dtype=torch.int32, device=dev),
+                   al=dict(sorted_pair=torch.empty(cap, dtype=torch.int32, device=dev),
+                           block_slot=torch.empty(cap // bm, dtype=torch.int32, device=dev),
+                           counts=torch.empty(E, dtype=torch.int32, device=dev),
+                           seg_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                           n_padded=torch.empty(1, dtype=torch.int32, device=dev)),
+                   aws=torch.empty(max(1, moe.align_workspace_bytes(T, k, E, bm)), dtype=torch.uint8, device=dev),
+                   fws=torch.empty(max(1, moe.ffn_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
+                                   device=dev),
+                   out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+        layers.append((li, pool, x, logits, soe, mask, buf))
+    del bdev
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name} T={T} layers={L} act={act} block_m={bm}: inputs ready in {time.time() - t0:.1f}s")
+
+    def run_layer(entry, stream):
+        li, pool, x, logits, soe, mask, b = entry
+        moe.route(logits, k, mask=mask, ids=b["ids"], w=b["w"], err=b["err"], stream=stream)
+        moe.align(b["ids"], E, bm, soe, out=b["al"], err=b["err"], ws=b["aws"] if b["aws"].numel() > 1 else None,
+                  stream=stream)
+        moe.expert_ffn(pool, x, k, E, b["w"], b["al"], bm, act, out=b["out"], ws=b["fws"], stream=stream)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+
+    def step():
+        for entry in layers:
+            run_layer(entry, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tok_s = T * L / (ms_step / 1e3)          # expert-layer tokens per second
+    log(f"[bench] {ms_step:.4f} ms/step, {ms_step / L * 1e3:.2f} us/layer (wall {wall:.3f}s)")
+
+    # ---- per-kernel durations with the library's event tracing, same steps eagerly
+    moe.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = moe.profile_read()
+    moe.profile_enable(False)
+    log("[bench] kernels: " + ", ".join(f"{n}: {c} x {ms / c * 1e3:.2f} us" for n, (c, ms) in prof.items()))
+
+    # ---- algorithmic work per layer
+    slot_used = {0: moe.slot_bytes(H, I, 0), 1: moe.slot_bytes(H, I, 1) if I % 128 == 0 else 0}
+    w13_bytes = {0: 2 * I * H + 8 * I, 1: I * H + 2 * I * (H // 128) * 4}
+    w2_bytes = {0: H * I + 4 * H, 1: H * I // 2 + H * (I // 128) * 4}
+    tot_bytes = tot_flops = g1_bytes = g2_bytes = 0
+    distinct = []
+    for li, pool, x, logits, soe, mask, b in layers:
+        ids = b["ids"].cpu().numpy()
+        used = np.unique(ids[ids >= 0])
+        distinct.append(used.size)
+        fm = li.expert_fmt[used]
+        w13 = sum(w13_bytes[int(f)] for f in fm)
+        w2 = sum(w2_bytes[int(f)] for f in fm)
+        NP = T * k
+        tot_bytes += w13 + w2 + T * H * 2 + T * E * 4 + T * H * 2 + NP * 16
+        tot_flops += 6 * NP * H * I
+        g1_bytes += w13 + T * H * 2 + NP * I * 2
+        g2_bytes += w2 + NP * I * 2 + T * H * 2
+    layer_s = ms_step / 1e3 / L
+    hbm_frac_layer = tot_bytes / L / layer_s / (HBM_PEAK_GBS * 1e9)
+    if act == moe.ACT_BF16:
+        dom = "gemm1_stream"
+        n, ms = prof[dom]
+        achieved = g1_bytes / n / (ms / n / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+        dtype = "bf16"
+    else:
+        dom = "gemm1_fp8"
+        n, ms = prof[dom]
+        flops = 4 * T * k * H * I * L
+        achieved = flops / n / (ms / n / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / FP8_PEAK_TFLOPS, 4))
+        dtype = "fp8"
+    roof["kernel"] = dom
+    roof["avg_us"] = round(ms / n * 1e3, 3)
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath)).get(f"{cfg.name}-T{T}-{dom}")
+        if rec and rec.get("source_hash") == source_hash("ffn_stream.hip" if act == moe.ACT_BF16 else "ffn_grouped.hip"):
+            traffic = rec.get("bytes_per_launch")
+    roof["traffic"] = traffic
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same layers
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle  # noqa: F401
+        threads = len(os.sched_getaffinity(0))
+        done_tok, t_cpu, n_layers = 0, 0.0, 0
+        sample_tokens = None if T <= 64 else np.arange(min(T, 16))
+        for li, *_ in layers:
+            c0 = time.perf_counter()
+            oracle_layer(li, bank, bm, act, token_subset=sample_tokens)
+            t_cpu += time.perf_counter() - c0
+            done_tok += T if sample_tokens is None else sample_tokens.size
+            n_layers += 1
+            if t_cpu >= args.cpu_seconds:
+                break
+        what = (f"{n_layers} of {L} layers, all {T} tokens each" if sample_tokens is None else
+                f"{n_layers} layers, {sample_tokens.size} of {T} tokens each (route and align run on all)")
+        cpu = dict(value=round(done_tok / t_cpu, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"{what}; fp64 NumPy incl. slot dequant; {t_cpu:.1f}s")
+        log(f"[bench] cpu oracle {cpu['value']} tokens/s over {t_cpu:.1f}s")
+
+    res = {
+        "metric": "MoE expert-layer tokens/s (layer tokens per second over the layer stack)",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} tokens x {L} layers, H={H}, I={I}, E={E}, top-{k}, "
+                               f"{'per-layer slot pools' if cfg.slots else 'all experts resident'}, "
+                               f"{'FP8 + int4' if cfg.int4_frac else 'FP8'} slots",
+                   "tokens_per_layer": T, "layers": L, "block_m": bm,
+                   "act_mode": "bf16" if act == moe.ACT_BF16 else "fp8_g128_pow2",
+                   "graph": graph is not None, "distinct_experts_per_layer": round(float(np.mean(distinct)), 1),
+                   "layer_us": round(layer_s * 1e6, 3), "layer_hbm_frac": round(hbm_frac_layer, 4),
+                   "layer_tflops": round(tot_flops / L / layer_s / 1e12, 2)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * moe.h -- C ABI of the MoE expert layer for MI355X (gfx950).
+ *
+ * One MoE layer on one GPU: fp32 router logits -> top-k route -> align
+ * (stable counting sort of token-expert pairs into per-expert segments padded
+ * to the GEMM tile, with the expert -> slot indirection) -> per-expert SwiGLU
+ * FFN reading FP8 or int4 expert weights from a per-layer VRAM slot pool ->
+ * weighted combine.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [PW]  "PagedWeight: Efficient MoE LLM Serving with Dynamic Quality-Aware
+ *        Weight Quantization", spectral-agent.com commentary.
+ *  [MG]  MOE-GEN explainer, aibr.jp.
+ *  [VEP] "vllm-expert-pager" article, rand.pepabo.com.
+ *
+ * Conventions for every call:
+ *  - Pointers named d_* are device memory owned by the caller; the library
+ *    borrows them for the call and keeps no reference afterwards.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the default stream). They never synchronise and never allocate device
+ *    memory; scratch memory is the caller's workspace argument.
+ *  - Return MOE_OK (0) or a negative status. MOE_EINVAL: a host-side argument
+ *    is invalid (null pointer, size out of range, workspace too small);
+ *    nothing was launched. MOE_EHIP: a launch failed; moe_last_hip_error()
+ *    gives the hipError_t value.
+ *  - Problems only the device can see are added to the caller's int32 error
+ *    word d_err (the caller zeroes it); the pairs concerned contribute zero
+ *    to the output and the call still completes.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EHIP = -2 };
+
+/* Slot storage formats ([PW] "technically interesting points": each expert is
+ * held at its own bit width; [VEP] introduction: official FP8 weights). */
+enum { MOE_FMT_FP8_E4M3_ROW = 0, /* OCP e4m3fn codes, one fp32 scale per row   */
+       MOE_FMT_INT4_G128 = 1 };  /* uint4, fp16 (scale, zero) per 128 along K */
+
+/* Activation precision of the expert FFN (the pages fix none):
+ *  MOE_ACT_BF16: token rows enter the contraction exactly (bf16), fp32
+ *    accumulate; the intermediate h is rounded to bf16. Needs T <= 64.
+ *  MOE_ACT_FP8_G128_POW2: token rows and h are quantized to e4m3 with one
+ *    power-of-two scale per (row, 128 consecutive K elements), the smallest
+ *    2^s with max|v| <= 448 * 2^s; FP8 matrix cores, fp32 accumulate. */
+enum { MOE_ACT_BF16 = 0, MOE_ACT_FP8_G128_POW2 = 1 };
+
+int         moe_abi_version(void);
+const char* moe_strerror(int status);
+int         moe_last_hip_error(void);
+
+/* ---------------------------------------------------------------- route
+ * [PW] "what was released" / "technically interesting points": a router
+ * sends each token to a few experts. Per token t: experts with mask[e] == 0
+ * count as -inf; the k chosen are the first k in the order (logit desc,
+ * expert id asc), with -0.0 == +0.0; weights are the softmax over the k
+ * chosen logits (they sum to 1), computed in fp32.
+ *  d_logits  f32 [T, E] row-major.
+ *  d_mask    u8 [E] or NULL (all experts allowed).
+ *  d_topk_ids i32 [T, k], best first; d_topk_w f32 [T, k].
+ *  d_err     i32 [1]: +1 per token with fewer than k allowed experts; such a
+ *            token's missing entries get id -1 and weight 0.
+ * Limits: 1 <= T, 1 <= k <= min(E, 32), E <= 1024. */
+int moe_route(const float* d_logits, const uint8_t* d_mask, int T, int E, int k,
+              int32_t* d_topk_ids, float* d_topk_w, int32_t* d_err, void* stream);
+
+/* ---------------------------------------------------------------- align
+ * [MG] sections 1 and 3: tokens are grouped per expert module so each expert
+ * runs one large batch. [VEP] "hierarchical paging of expert weights": each
+ * layer keeps a table of which expert sits in which VRAM slot.
+ * Pair p = t*k + j. Segments in ascending expert id, pairs inside a segment
+ * in ascending p, each segment padded to a multiple of block_m with the
+ * sentinel T*k; an expert without pairs has no block.
+ *  d_sorted_pair  i32 [capacity]; entries [0, n_padded) are defined.
+ *  d_block_slot   i32 [capacity / block_m]; entry b is slot_of_expert[e] of
+ *                 the expert owning block b (-1 if not resident).
+ *  d_counts i32 [E]; d_seg_offset i32 [E + 1] (padded starts; [E] = n_padded);
+ *  d_n_padded i32 [1].
+ *  d_err i32 [1]: + number of pairs whose id is outside [0, E) (they are
+ *        left out) + number of pairs routed to a non-resident expert.
+ * block_m in {16, 32, 64, 128, 256}; E <= 1024; T*k < 2^30.
+ * The results are bit-identical from run to run. */
+int    moe_align_capacity(int T, int k, int E, int block_m);
+size_t moe_align_workspace_bytes(int T, int k, int E, int block_m);
+int moe_align(const int32_t* d_topk_ids, int T, int k, int E, int block_m,
+              const int32_t* d_slot_of_expert,
+              int32_t* d_sorted_pair, int32_t* d_block_slot, int32_t* d_counts,
+              int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err,
+              void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- slot pool
+ * [VEP] "hierarchical paging of expert weights": each MoE layer owns a pool
+ * of VRAM slots, one expert per slot; the Table 1 set-up names the fused
+ * gate+up tensor w13_weight and the down tensor w2_weight.
+ * Slot s starts at d_base + s * slot_bytes. Inside a slot each array starts
+ * on a 256-byte boundary, in this order:
+ *  FP8 : w13 codes u8[2I][H] | w13 scale f32[2I] | w2 codes u8[H][I] | w2 scale f32[H]
+ *  INT4: w13 u8[2I][H/2] | w13 (scale, zero) f16[2I][H/128][2]
+ *        | w2 u8[H][I/2] | w2 (scale, zero) f16[H][I/128][2]
+ *        element c of a row: low nibble of byte c/2 if c is even, else high.
+ *  Dequantized: FP8 W[r][c] = e4m3(q[r][c]) * scale[r];
+ *               INT4 W[r][c] = (q[r][c] - zero[r][c/128]) * scale[r][c/128].
+ * Rows [0, I) of w13 are the gate projection, rows [I, 2I) the up projection.
+ * d_slot_fmt is a device array u8[n_slots] of MOE_FMT_* values.
+ * hidden % 128 == 0, inter % 64 == 0 (INT4 slots: inter % 128 == 0). */
+typedef struct moe_slot_pool {
+    void*          d_base;
+    size_t         slot_bytes;   /* >= moe_slot_bytes of every format used, multiple of 256 */
+    int            n_slots;
+    const uint8_t* d_slot_fmt;
+    int            hidden;
+    int            inter;
+} moe_slot_pool;
+
+size_t moe_slot_bytes(int hidden, int inter, int fmt);
+/* byte offset of array `part` (0..3 in the order above) inside a slot */
+size_t moe_slot_part_offset(int hidden, int inter, int fmt, int part);
+
+/* ---------------------------------------------------------------- expert FFN
+ * [VEP] Table 1 set-up and "hierarchical paging" section: the expert's w13
+ * and w2 are read from its slot; [PW] "what was released": the layer output
+ * mixes the chosen experts' outputs. For every pair p = t*k + j listed in
+ * block b (slot s = block_slot[b], skipped if s < 0):
+ *    gu = W13[s] a_t, h = silu(gu[0:I]) * gu[I:2I], y = W2[s] h,
+ *    out[t] = sum_j topk_w[t][j] * y_(t,j), accumulated in fp32, then bf16.
+ * a_t is token row t of x in the precision act_mode selects.
+ *  d_x bf16 [T, H]; d_topk_w f32 [T, k]; d_sorted_pair, d_block_slot,
+ *  d_n_padded as written by moe_align with the same block_m and E.
+ *  d_out bf16 [T, H], fully overwritten (rows of tokens with no resident
+ *  expert are zero).
+ * block_m: 16, 32 or 64 with MOE_ACT_BF16; 64 or 128 with
+ * MOE_ACT_FP8_G128_POW2. The workspace holds moe_ffn_workspace_bytes bytes. */
+size_t moe_ffn_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode);
+int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E,
+                   const float* d_topk_w, const int32_t* d_sorted_pair,
+                   const int32_t* d_block_slot, const int32_t* d_n_padded,
+                   int block_m, int act_mode, uint16_t* d_out,
+                   void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- dequant
+ * [PW] "technically interesting points": per-expert bit width. Writes the
+ * dequantized matrices of slot `slot` in fp32: d_w13 [2I][H], d_w2 [H][I]
+ * (either may be NULL). */
+int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream);
+
+/* ---------------------------------------------------------------- tracing
+ * Launch tracing for measurement (the MOE-GEN explainer, aibr.jp, section 2
+ * and its closing checklist, asks for GPU utilisation and throughput figures
+ * per module). moe_profile_enable(1) clears old records and brackets every
+ * later kernel launch of the library with two HIP events on its stream (not
+ * while a stream is being captured); moe_profile_enable(0) stops and frees
+ * the events. moe_profile_read() waits for the recorded events of kernel
+ * `kernel` (0 <= kernel < moe_profile_kernels(); names from
+ * moe_profile_kernel_name) and returns the launch count and the summed
+ * milliseconds. Not thread-safe. */
+int         moe_profile_enable(int on);
+int         moe_profile_kernels(void);
+const char* moe_profile_kernel_name(int kernel);
+int         moe_profile_read(int kernel, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

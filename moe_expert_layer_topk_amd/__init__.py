@@ -1,0 +1,10 @@
+"""MoE expert layer for MI355X (gfx950): route -> align -> paged-slot SwiGLU FFN.
+
+The compute lives in libmoe.so (hand-written HIP, C ABI in include/moe.h);
+this package is the thin Python binding over it.
+"""
+from .binding import (  # noqa: F401
+    MoeError, SlotPool, route, align, align_capacity, align_workspace_bytes, expert_ffn,
+    ffn_workspace_bytes, dequant_slot, slot_bytes, slot_part_offset, layer, lib, declared_symbols,
+    LIB_PATH, profile_enable, profile_read, ACT_BF16, ACT_FP8_G128_POW2, FMT_FP8_E4M3_ROW, FMT_INT4_G128,
+)

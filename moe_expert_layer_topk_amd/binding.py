@@ -1,0 +1,255 @@
+"""ctypes binding over libmoe.so (include/moe.h): argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels. PyTorch supplies
+device memory and the current stream; outputs the caller does not pass are
+allocated with torch before the call. If the library is missing the first
+call raises: there is no other implementation to fall back to.
+"""
+import ctypes
+import os
+import re
+from ctypes import c_int, c_size_t, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_EHIP = 0, -1, -2
+FMT_FP8_E4M3_ROW, FMT_INT4_G128 = 0, 1
+ACT_BF16, ACT_FP8_G128_POW2 = 0, 1
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class moe_slot_pool(ctypes.Structure):
+    _fields_ = [("d_base", c_void_p), ("slot_bytes", c_size_t), ("n_slots", c_int),
+                ("d_slot_fmt", c_void_p), ("hidden", c_int), ("inter", c_int)]
+
+
+_lib = None
+
+
+def _declare(lib):
+    P = c_void_p
+    sig = {
+        "moe_abi_version": (c_int, []),
+        "moe_strerror": (ctypes.c_char_p, [c_int]),
+        "moe_last_hip_error": (c_int, []),
+        "moe_route": (c_int, [P, P, c_int, c_int, c_int, P, P, P, P]),
+        "moe_align_capacity": (c_int, [c_int, c_int, c_int, c_int]),
+        "moe_align_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "moe_align": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P, P, c_size_t, P]),
+        "moe_slot_bytes": (c_size_t, [c_int, c_int, c_int]),
+        "moe_slot_part_offset": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+        "moe_expert_ffn": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
+                                   c_int, c_int, P, P, c_size_t, P]),
+        "moe_dequant_slot": (c_int, [ctypes.POINTER(moe_slot_pool), c_int, P, P, P]),
+        "moe_profile_enable": (c_int, [c_int]),
+        "moe_profile_kernels": (c_int, []),
+        "moe_profile_kernel_name": (ctypes.c_char_p, [c_int]),
+        "moe_profile_read": (c_int, [c_int, ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(python -m moe_expert_layer_topk_amd.build)")
+        # torch ships its own HIP runtime (same soname as ROCm's). Load torch
+        # first so the library binds to that runtime instead of pulling in a
+        # second one, which would see no device.
+        import torch  # noqa: F401
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declared_symbols():
+    """Function names declared in include/moe.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status):
+    if status != MOE_OK:
+        L = lib()
+        msg = L.moe_strerror(status).decode()
+        raise MoeError(f"libmoe: {msg} (status {status}, hip error {L.moe_last_hip_error()})")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, dtype=None, numel=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise MoeError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------- route
+def route(logits, k, mask=None, ids=None, w=None, err=None, stream=None):
+    import torch
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _check(lib().moe_route(_ptr(logits, torch.float32, T * E, "logits"),
+                           _ptr(mask, torch.uint8, E, "mask"), T, E, k,
+                           _ptr(ids, torch.int32, T * k, "ids"), _ptr(w, torch.float32, T * k, "w"),
+                           _ptr(err, torch.int32, 1, "err"), _stream(stream)))
+    return ids, w, err
+
+
+# ---------------------------------------------------------------- align
+def align_capacity(T, k, E, block_m):
+    cap = lib().moe_align_capacity(T, k, E, block_m)
+    if cap < 0:
+        _check(cap)
+    return cap
+
+
+def align_workspace_bytes(T, k, E, block_m):
+    return int(lib().moe_align_workspace_bytes(T, k, E, block_m))
+
+
+def align(ids, E, block_m, slot_of_expert, out=None, err=None, ws=None, stream=None):
+    """Returns dict(sorted_pair, block_slot, counts, seg_offset, n_padded, err)."""
+    import torch
+    T, k = ids.shape
+    dev = ids.device
+    cap = align_capacity(T, k, E, block_m)
+    if out is None:
+        out = dict(sorted_pair=torch.empty(cap, dtype=torch.int32, device=dev),
+                   block_slot=torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+                   counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   seg_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   n_padded=torch.empty(1, dtype=torch.int32, device=dev))
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    need = align_workspace_bytes(T, k, E, block_m)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_align(_ptr(ids, torch.int32, T * k, "ids"), T, k, E, block_m,
+                           _ptr(slot_of_expert, torch.int32, E, "slot_of_expert"),
+                           _ptr(out["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                           _ptr(out["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                           _ptr(out["counts"], torch.int32, E, "counts"),
+                           _ptr(out["seg_offset"], torch.int32, E + 1, "seg_offset"),
+                           _ptr(out["n_padded"], torch.int32, 1, "n_padded"),
+                           _ptr(err, torch.int32, 1, "err"),
+                           _ptr(ws, torch.uint8, need, "ws") if need else None,
+                           c_size_t(need), _stream(stream)))
+    out = dict(out)
+    out["err"] = err
+    return out
+
+
+# ---------------------------------------------------------------- slot pool
+def slot_bytes(hidden, inter, fmt):
+    return int(lib().moe_slot_bytes(hidden, inter, fmt))
+
+
+def slot_part_offset(hidden, inter, fmt, part):
+    return int(lib().moe_slot_part_offset(hidden, inter, fmt, part))
+
+
+class SlotPool:
+    """A layer's VRAM slot pool: uint8 device tensor [n_slots, stride] plus the
+    per-slot format tags (device uint8 [n_slots])."""
+
+    def __init__(self, data, fmt, hidden, inter):
+        self.data, self.fmt, self.hidden, self.inter = data, fmt, hidden, inter
+        self._c = moe_slot_pool(c_void_p(data.data_ptr()), data.shape[1], data.shape[0],
+                                c_void_p(fmt.data_ptr()), hidden, inter)
+
+    @property
+    def n_slots(self):
+        return self.data.shape[0]
+
+    def c_ref(self):
+        return ctypes.byref(self._c)
+
+
+# ---------------------------------------------------------------- expert FFN
+def ffn_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode):
+    return int(lib().moe_ffn_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode))
+
+
+def expert_ffn(pool, x, k, E, topk_w, aligned, block_m, act_mode, out=None, ws=None, stream=None):
+    import torch
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    need = ffn_workspace_bytes(T, k, E, pool.hidden, pool.inter, block_m, act_mode)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    cap = align_capacity(T, k, E, block_m)
+    _check(lib().moe_expert_ffn(pool.c_ref(), _ptr(x, torch.bfloat16, T * H, "x"), T, k, E,
+                                _ptr(topk_w, torch.float32, T * k, "topk_w"),
+                                _ptr(aligned["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                                _ptr(aligned["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                                _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
+                                block_m, act_mode, _ptr(out, torch.bfloat16, T * H, "out"),
+                                _ptr(ws, torch.uint8, need, "ws"), c_size_t(ws.numel()), _stream(stream)))
+    return out
+
+
+def dequant_slot(pool, slot, w13=None, w2=None, stream=None):
+    import torch
+    H, I = pool.hidden, pool.inter
+    dev = pool.data.device
+    w13 = torch.empty((2 * I, H), dtype=torch.float32, device=dev) if w13 is None else w13
+    w2 = torch.empty((H, I), dtype=torch.float32, device=dev) if w2 is None else w2
+    _check(lib().moe_dequant_slot(pool.c_ref(), slot, _ptr(w13, torch.float32, 2 * I * H, "w13"),
+                                  _ptr(w2, torch.float32, H * I, "w2"), _stream(stream)))
+    return w13, w2
+
+
+# ---------------------------------------------------------------- tracing
+def profile_enable(on=True):
+    _check(lib().moe_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """{kernel name: (launches, total ms)} for kernels launched since enable."""
+    L = lib()
+    out = {}
+    for i in range(L.moe_profile_kernels()):
+        n, ms = c_int(0), ctypes.c_double(0.0)
+        _check(L.moe_profile_read(i, ctypes.byref(n), ctypes.byref(ms)))
+        if n.value:
+            out[L.moe_profile_kernel_name(i).decode()] = (n.value, ms.value)
+    return out
+
+
+# ---------------------------------------------------------------- whole layer
+def layer(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, stream=None):
+    """route -> align -> expert FFN on one stream; returns (out, route, align)."""
+    E = logits.shape[1]
+    ids, w, rerr = route(logits, k, mask=mask, stream=stream)
+    al = align(ids, E, block_m, slot_of_expert, stream=stream)
+    out = expert_ffn(pool, x, k, E, w, al, block_m, act_mode, stream=stream)
+    return out, (ids, w, rerr), al

@@ -1,0 +1,190 @@
+// extern "C" boundary of libmoe: argument checks, workspace carving and
+// dispatch to the gfx950 kernels. Declarations and contracts: include/moe.h.
+#include "../../include/moe.h"
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// hipGetLastError() reports the last error of any runtime call on the thread,
+// including the caller's own earlier calls; clear it before launching so a
+// stale value is not taken for a failure of ours.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    g_last_hip = (int)e;
+    return MOE_EHIP;
+}
+
+size_t up256(size_t n) { return (n + 255) / 256 * 256; }
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+// Byte offsets of the four arrays of a slot (each 256-byte aligned).
+void slot_parts(int H, int I, int fmt, size_t off[4], size_t* total) {
+    size_t sz[4];
+    if (fmt == MOE_FMT_FP8_E4M3_ROW) {
+        sz[0] = (size_t)2 * I * H;
+        sz[1] = (size_t)2 * I * 4;
+        sz[2] = (size_t)H * I;
+        sz[3] = (size_t)H * 4;
+    } else {
+        sz[0] = (size_t)I * H;
+        sz[1] = (size_t)2 * I * (H / 128) * 4;
+        sz[2] = (size_t)H * I / 2;
+        sz[3] = (size_t)H * (I / 128) * 4;
+    }
+    size_t o = 0;
+    for (int i = 0; i < 4; ++i) {
+        off[i] = o;
+        o = up256(o + sz[i]);
+    }
+    if (total) *total = o;
+}
+
+bool pool_args(const moe_slot_pool* pool, moe::PoolArgs* pa) {
+    if (!pool || !pool->d_base || !pool->d_slot_fmt || pool->n_slots < 1) return false;
+    const int H = pool->hidden, I = pool->inter;
+    if (H < 128 || H % 128 || I < 64 || I % 64) return false;
+    size_t fp8_bytes, int4_bytes = 0;
+    slot_parts(H, I, MOE_FMT_FP8_E4M3_ROW, pa->off[0], &fp8_bytes);
+    if (I % 128 == 0) {
+        slot_parts(H, I, MOE_FMT_INT4_G128, pa->off[1], &int4_bytes);
+    } else {
+        for (int i = 0; i < 4; ++i) pa->off[1][i] = pa->off[0][i];   // int4 slots need inter % 128 == 0
+    }
+    // The formats live on the device; the stride must at least hold the
+    // smallest format (the caller guarantees it holds every format it uses).
+    const size_t smallest = int4_bytes ? int4_bytes : fp8_bytes;
+    if (pool->slot_bytes % 256 || pool->slot_bytes < smallest) return false;
+    pa->base = pool->d_base;
+    pa->stride = pool->slot_bytes;
+    pa->fmt = pool->d_slot_fmt;
+    pa->hidden = H;
+    pa->inter = I;
+    return true;
+}
+
+int capacity(int T, int k, int E, int bm) {
+    long long np = (long long)T * k;
+    long long n = np + (np < E ? np : E) * (long long)(bm - 1);
+    return (int)((n + bm - 1) / bm * bm);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int moe_last_hip_error(void) { return g_last_hip; }
+
+int moe_route(const float* d_logits, const uint8_t* d_mask, int T, int E, int k, int32_t* d_topk_ids,
+              float* d_topk_w, int32_t* d_err, void* stream) {
+    if (!d_logits || !d_topk_ids || !d_topk_w || !d_err) return MOE_EINVAL;
+    if (T < 1 || E < 1 || E > MOE_MAX_E || k < 1 || k > E || k > MOE_MAX_K) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_route(d_logits, d_mask, T, E, k, d_topk_ids, d_topk_w, d_err, (hipStream_t)stream));
+}
+
+int moe_align_capacity(int T, int k, int E, int block_m) {
+    if (T < 1 || k < 1 || E < 1 || !valid_block_m(block_m)) return MOE_EINVAL;
+    if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
+    return capacity(T, k, E, block_m);
+}
+
+size_t moe_align_workspace_bytes(int T, int k, int E, int block_m) {
+    if (T < 1 || k < 1 || E < 1 || E > MOE_MAX_E || !valid_block_m(block_m)) return 0;
+    return moe::align_workspace_bytes(T * k, E);
+}
+
+int moe_align(const int32_t* d_topk_ids, int T, int k, int E, int block_m, const int32_t* d_slot_of_expert,
+              int32_t* d_sorted_pair, int32_t* d_block_slot, int32_t* d_counts, int32_t* d_seg_offset,
+              int32_t* d_n_padded, int32_t* d_err, void* d_ws, size_t ws_bytes, void* stream) {
+    if (!d_topk_ids || !d_slot_of_expert || !d_sorted_pair || !d_block_slot || !d_counts || !d_seg_offset ||
+        !d_n_padded || !d_err)
+        return MOE_EINVAL;
+    if (T < 1 || k < 1 || E < 1 || E > MOE_MAX_E || !valid_block_m(block_m)) return MOE_EINVAL;
+    if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
+    size_t need = moe::align_workspace_bytes(T * k, E);
+    if (need && (!d_ws || ws_bytes < need)) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_align(d_topk_ids, T * k, E, block_m, d_slot_of_expert, d_sorted_pair, d_block_slot,
+                                        d_counts, d_seg_offset, d_n_padded, d_err, d_ws, (hipStream_t)stream));
+}
+
+size_t moe_slot_bytes(int hidden, int inter, int fmt) {
+    if (hidden < 128 || hidden % 128 || inter < 64 || inter % 64) return 0;
+    if (fmt != MOE_FMT_FP8_E4M3_ROW && fmt != MOE_FMT_INT4_G128) return 0;
+    if (fmt == MOE_FMT_INT4_G128 && inter % 128) return 0;
+    size_t off[4], total;
+    slot_parts(hidden, inter, fmt, off, &total);
+    return total;
+}
+
+size_t moe_slot_part_offset(int hidden, int inter, int fmt, int part) {
+    if (part < 0 || part > 3 || moe_slot_bytes(hidden, inter, fmt) == 0) return (size_t)-1;
+    size_t off[4], total;
+    slot_parts(hidden, inter, fmt, off, &total);
+    return off[part];
+}
+
+size_t moe_ffn_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode) {
+    if (T < 1 || k < 1 || E < 1 || !valid_block_m(block_m)) return 0;
+    const int cap = capacity(T, k, E, block_m);
+    if (act_mode == MOE_ACT_BF16) return moe::stream_workspace_bytes(cap, inter);
+    if (act_mode == MOE_ACT_FP8_G128_POW2) return moe::grouped_workspace_bytes(T, k, hidden, inter, cap);
+    return 0;
+}
+
+int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E, const float* d_topk_w,
+                   const int32_t* d_sorted_pair, const int32_t* d_block_slot, const int32_t* d_n_padded,
+                   int block_m, int act_mode, uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+    moe::PoolArgs pa;
+    if (!pool_args(pool, &pa)) return MOE_EINVAL;
+    if (!d_x || !d_topk_w || !d_sorted_pair || !d_block_slot || !d_n_padded || !d_out || !d_ws) return MOE_EINVAL;
+    if (T < 1 || k < 1 || E < 1 || E > MOE_MAX_E || k > E) return MOE_EINVAL;
+    if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
+    const int cap = capacity(T, k, E, block_m < 1 ? 1 : block_m);
+    if (act_mode == MOE_ACT_BF16) {
+        if (block_m != 16 && block_m != 32 && block_m != 64) return MOE_EINVAL;
+        if (T > moe::stream_max_tokens()) return MOE_EINVAL;
+        if (ws_bytes < moe::stream_workspace_bytes(cap, pa.inter)) return MOE_EINVAL;
+        clear_stale_error();
+    return hip_status(moe::launch_ffn_stream(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
+                                                 cap, block_m, d_out, d_ws, (hipStream_t)stream));
+    }
+    if (act_mode == MOE_ACT_FP8_G128_POW2) {
+        if (block_m != 64 && block_m != 128) return MOE_EINVAL;
+        if (ws_bytes < moe::grouped_workspace_bytes(T, k, pa.hidden, pa.inter, cap)) return MOE_EINVAL;
+        clear_stale_error();
+    return hip_status(moe::launch_ffn_grouped(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
+                                                  cap, block_m, d_out, d_ws, (hipStream_t)stream));
+    }
+    return MOE_EINVAL;
+}
+
+int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream) {
+    moe::PoolArgs pa;
+    if (!pool_args(pool, &pa)) return MOE_EINVAL;
+    if (slot < 0 || slot >= pool->n_slots) return MOE_EINVAL;
+    if (!d_w13 && !d_w2) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_dequant(pa, slot, d_w13, d_w2, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+// Align: stable counting sort of token-expert pairs into per-expert segments
+// padded to the GEMM tile, plus the expert -> slot indirection.
+//
+// MOE-GEN explainer (aibr.jp), sections 1 and 3: tokens are grouped per
+// expert so each expert runs one large batch. vllm-expert-pager article
+// (rand.pepabo.com), "hierarchical paging of expert weights": a per-layer
+// table says which VRAM slot holds which expert.
+//
+// Positions come from counts and wavefront ranks only (ballot / popcount
+// matching), never from the order in which atomics land, so every output is
+// identical from run to run.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int ALIGN_THREADS = 1024;              // 16 waves
+constexpr int ALIGN_WAVES = ALIGN_THREADS / MOE_WAVE;
+constexpr int ALIGN_CHUNK = 4096;                // pairs per block in the multi-block path
+
+// Lanes of the wave that hold the same key (keys < 2048; -1 = no key).
+__device__ __forceinline__ uint64_t match_peers(int key) {
+    uint64_t peers = __ballot(key >= 0);
+    peers = key >= 0 ? peers : ~peers;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+        uint64_t m = __ballot((key >> b) & 1);
+        peers &= ((key >> b) & 1) ? m : ~m;
+    }
+    return peers;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim == ALIGN_THREADS).
+__device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
+    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == MOE_WAVE - 1) s_tmp[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+        int s = lane < ALIGN_WAVES ? s_tmp[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < MOE_WAVE; o <<= 1) {
+            int y = __shfl_up(s, o, 64);
+            if (lane >= o) s += y;
+        }
+        if (lane < ALIGN_WAVES) s_tmp[ALIGN_WAVES + lane] = s;   // inclusive wave totals
+    }
+    __syncthreads();
+    int wave_base = wv == 0 ? 0 : s_tmp[ALIGN_WAVES + wv - 1];
+    total = s_tmp[2 * ALIGN_WAVES - 1];
+    __syncthreads();
+    return wave_base + x - v;
+}
+
+// From per-expert counts: padded offsets, n_padded, block -> slot map, the
+// sentinel padding of every segment tail, and the non-resident pair count.
+// One block of ALIGN_THREADS threads; counts in s_cnt[E].
+__device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_tmp, int E, int block_m, int sentinel,
+                                     const int32_t* slot_of_expert, int32_t* counts, int32_t* seg_offset,
+                                     int32_t* n_padded, int32_t* block_slot, int32_t* sorted_pair, int32_t* err) {
+    const int e = threadIdx.x;
+    int c = e < E ? s_cnt[e] : 0;
+    int padded = (c + block_m - 1) / block_m * block_m;
+    int total;
+    int off = block_exclusive_scan(padded, s_tmp, total);
+    if (e < E) {
+        s_off[e] = off;
+        counts[e] = c;
+        seg_offset[e] = off;
+        int slot = slot_of_expert[e];
+        for (int b = off / block_m; b < (off + padded) / block_m; ++b) block_slot[b] = slot;
+        for (int q = off + c; q < off + padded; ++q) sorted_pair[q] = sentinel;
+        if (slot < 0 && c > 0) atomicAdd(err, c);
+    }
+    if (e == 0) {
+        seg_offset[E] = total;
+        *n_padded = total;
+    }
+    __syncthreads();
+}
+
+// Scatter pairs [p0, p1) in ascending order; s_run[e] holds the next free
+// position of expert e and is advanced. The pairs are taken in rounds of
+// ALIGN_THREADS; inside a round, wave w's pairs of expert e are placed after
+// those of waves < w (wave counts in s_wcnt[w][e]).
+__device__ void scatter_pairs(const int32_t* ids, int p0, int p1, int E, int* s_run, uint8_t* s_wcnt,
+                              int32_t* sorted_pair) {
+    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
+    for (int base = p0; base < p1; base += ALIGN_THREADS) {
+        for (int i = threadIdx.x; i < ALIGN_WAVES * E; i += ALIGN_THREADS) s_wcnt[i] = 0;
+        __syncthreads();
+        int p = base + threadIdx.x;
+        int e = p < p1 ? ids[p] : -1;
+        if (e >= E) e = -1;
+        uint64_t peers = match_peers(e);
+        int rank = __popcll(peers & lanemask_lt());
+        bool leader = e >= 0 && (peers & lanemask_lt()) == 0;
+        if (leader) s_wcnt[wv * E + e] = (uint8_t)__popcll(peers);
+        __syncthreads();
+        if (e >= 0) {
+            int before = 0;
+            for (int w2 = 0; w2 < wv; ++w2) before += s_wcnt[w2 * E + e];
+            sorted_pair[s_run[e] + before + rank] = p;
+        }
+        __syncthreads();
+        for (int x = threadIdx.x; x < E; x += ALIGN_THREADS) {
+            int add = 0;
+            for (int w2 = 0; w2 < ALIGN_WAVES; ++w2) add += s_wcnt[w2 * E + x];
+            s_run[x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+// Whole align in one block (small T*k).
+__global__ void __launch_bounds__(ALIGN_THREADS) align_single_kernel(
+    const int32_t* __restrict__ ids, int NP, int E, int block_m, const int32_t* __restrict__ slot_of_expert,
+    int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
+    int32_t* err) {
+    __shared__ int s_cnt[MOE_MAX_E];
+    __shared__ int s_run[MOE_MAX_E];
+    __shared__ int s_tmp[2 * ALIGN_WAVES];
+    __shared__ uint8_t s_wcnt[ALIGN_WAVES * MOE_MAX_E];
+    for (int i = threadIdx.x; i < E; i += ALIGN_THREADS) s_cnt[i] = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int p = threadIdx.x; p < NP; p += ALIGN_THREADS) {
+        int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+        else ++bad;
+    }
+    if (bad) atomicAdd(err, bad);
+    __syncthreads();
+    segments_from_counts(s_cnt, s_run, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
+                         block_slot, sorted_pair, err);
+    scatter_pairs(ids, 0, NP, E, s_run, s_wcnt, sorted_pair);
+}
+
+// Multi-block path: 1) per-chunk histograms, 2) one block turns them into
+// segments and per-chunk start positions, 3) each chunk scatters its pairs.
+__global__ void __launch_bounds__(256) align_hist_kernel(const int32_t* __restrict__ ids, int NP, int E,
+                                                        int32_t* __restrict__ hist, int32_t* err) {
+    __shared__ int s_cnt[MOE_MAX_E];
+    for (int i = threadIdx.x; i < E; i += blockDim.x) s_cnt[i] = 0;
+    __syncthreads();
+    int p0 = blockIdx.x * ALIGN_CHUNK, p1 = min(NP, p0 + ALIGN_CHUNK);
+    int bad = 0;
+    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+        int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+        else ++bad;
+    }
+    if (bad) atomicAdd(err, bad);
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += blockDim.x) hist[(size_t)blockIdx.x * E + i] = s_cnt[i];
+}
+
+__global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
+    int32_t* __restrict__ hist, int n_chunks, int NP, int E, int block_m,
+    const int32_t* __restrict__ slot_of_expert, int32_t* sorted_pair, int32_t* block_slot, int32_t* counts,
+    int32_t* seg_offset, int32_t* n_padded, int32_t* err) {
+    __shared__ int s_cnt[MOE_MAX_E];
+    __shared__ int s_off[MOE_MAX_E];
+    __shared__ int s_tmp[2 * ALIGN_WAVES];
+    const int e = threadIdx.x;
+    if (e < E) {
+        int c = 0;
+        for (int b = 0; b < n_chunks; ++b) c += hist[(size_t)b * E + e];
+        s_cnt[e] = c;
+    }
+    __syncthreads();
+    segments_from_counts(s_cnt, s_off, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
+                         block_slot, sorted_pair, err);
+    if (e < E) {                         // hist[b][e] <- start of chunk b's pairs of expert e
+        int run = s_off[e];
+        for (int b = 0; b < n_chunks; ++b) {
+            int c = hist[(size_t)b * E + e];
+            hist[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(ALIGN_THREADS) align_scatter_kernel(const int32_t* __restrict__ ids, int NP,
+                                                                     int E, const int32_t* __restrict__ start,
+                                                                     int32_t* sorted_pair) {
+    __shared__ int s_run[MOE_MAX_E];
+    __shared__ uint8_t s_wcnt[ALIGN_WAVES * MOE_MAX_E];
+    for (int i = threadIdx.x; i < E; i += ALIGN_THREADS) s_run[i] = start[(size_t)blockIdx.x * E + i];
+    __syncthreads();
+    int p0 = blockIdx.x * ALIGN_CHUNK, p1 = min(NP, p0 + ALIGN_CHUNK);
+    scatter_pairs(ids, p0, p1, E, s_run, s_wcnt, sorted_pair);
+}
+
+int align_single_max_pairs() { return 8192; }
+
+size_t align_workspace_bytes(int NP, int E) {
+    if (NP <= align_single_max_pairs()) return 0;
+    size_t chunks = (size_t)(NP + ALIGN_CHUNK - 1) / ALIGN_CHUNK;
+    return chunks * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_align(const int32_t* ids, int NP, int E, int block_m, const int32_t* slot_of_expert,
+                        int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset,
+                        int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream) {
+    if (NP <= align_single_max_pairs()) {
+        MOE_LAUNCH(K_ALIGN_SINGLE, stream, align_single_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, ids, NP, E, block_m,
+                           slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+        return hipGetLastError();
+    }
+    int chunks = (NP + ALIGN_CHUNK - 1) / ALIGN_CHUNK;
+    int32_t* hist = (int32_t*)ws;
+    MOE_LAUNCH(K_ALIGN_HIST, stream, align_hist_kernel, dim3(chunks), dim3(256), 0, stream, ids, NP, E, hist, err);
+    MOE_LAUNCH(K_ALIGN_SCAN, stream, align_scan_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, hist, chunks, NP, E, block_m,
+                       slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+    MOE_LAUNCH(K_ALIGN_SCATTER, stream, align_scatter_kernel, dim3(chunks), dim3(ALIGN_THREADS), 0, stream, ids, NP, E, hist,
+                       sorted_pair);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the gfx950 kernels of the expert layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+#define MOE_WAVE 64
+#define MOE_MAX_E 1024
+#define MOE_MAX_K 32
+#define MOE_ACT_G 128          // activation-scale group along K
+#define MOE_INT4_G 128         // int4 weight group along K
+
+namespace moe {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Smallest s with amax <= 448 * 2^s (s = 0 for amax == 0), exact: with
+// amax = m * 2^e, m in [0.5, 1) and 448 = 0.875 * 2^9.
+__device__ __forceinline__ int pow2_exponent_448(float amax) {
+    if (!(amax > 0.f)) return 0;
+    int e;
+    float m = frexpf(amax, &e);
+    return (m <= 0.875f) ? e - 9 : e - 8;
+}
+
+// two fp32 -> two OCP e4m3 codes packed in the low 16 bits (round to nearest even)
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// four e4m3 codes (one dword) -> four bf16 (two dwords); exact
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// wave-wide reductions (64 lanes)
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        uint64_t w = __shfl_xor(v, o, 64);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Matrix-core wrappers. Callers keep the whole wave active around them.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// A, B: 32 e4m3 codes per lane; sa, sb: E8M0 scale bytes (127 = 1.0)
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+}  // namespace moe

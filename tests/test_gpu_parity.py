@@ -1,0 +1,227 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer outputs (route ids, every align output) must be bit-exact; route
+weights within 1e-6; layer outputs within max|out - ref| <= 2e-2 * max|ref|
+against the fp64 oracle in the same activation mode.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import moe_expert_layer_topk_amd as moe
+from gen import CONFIGS, make_layer, make_bank
+from gen.configs import Config
+from harness import device_pool, device_inputs, oracle_layer, rel_max_err, bank_on_device
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+W_TOL = 1e-6
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def check_route(logits_np, mask_np, k, ids, w, err):
+    oi, ow, oe = oracle.route(logits_np, mask_np, k)
+    assert np.array_equal(ids.cpu().numpy(), oi), "route ids differ"
+    assert np.abs(w.cpu().numpy().astype(np.float64) - ow).max() <= W_TOL
+    assert int(err.item()) == oe
+
+
+def check_align(al, ref, block_m):
+    n = int(al["n_padded"].item())
+    assert n == ref["n_padded"]
+    assert np.array_equal(al["sorted_pair"][:n].cpu().numpy(), ref["sorted_pair"])
+    assert np.array_equal(al["block_slot"][:n // block_m].cpu().numpy(), ref["block_slot"])
+    assert np.array_equal(al["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(al["seg_offset"].cpu().numpy(), ref["seg_offset"])
+    assert int(al["err"].item()) == ref["err"]
+
+
+def run_layer(li, bank, dev, block_m, act_mode, sample=None, bank_dev=None, cache=None):
+    c = li.cfg
+    _say(f"[layer] {c.name} T={li.T} layer={li.layer} block_m={block_m} act={act_mode}")
+    pool = device_pool(li, bank, dev, bank_dev)
+    x, logits, soe, mask = device_inputs(li, dev)
+    out, (ids, w, rerr), al = moe.layer(pool, x, logits, c.k, soe, block_m, act_mode, mask=mask)
+    import torch
+    torch.cuda.synchronize()
+    ref = oracle_layer(li, bank, block_m, act_mode, token_subset=sample, cache=cache)
+    if sample is None:
+        check_route(li.logits, li.mask, c.k, ids, w, rerr)
+    else:
+        oi, ow, _ = oracle.route(li.logits[sample], li.mask, c.k)
+        assert np.array_equal(ids.cpu().numpy()[sample], oi)
+        assert np.abs(w.cpu().numpy()[sample].astype(np.float64) - ow).max() <= W_TOL
+    check_align(al, ref, block_m)
+    rows = None if sample is None else np.asarray(sample)
+    e = rel_max_err(out, ref["out"], rows)
+    _say(f"    rel max err {e:.3e}")
+    assert e <= OUT_TOL
+    return out, ref
+
+
+# ---------------------------------------------------------------- route
+def test_route_c0(gpu):
+    li = make_layer(CONFIGS["C0"], 16, 0)
+    x, logits, soe, mask = device_inputs(li, gpu)
+    ids, w, err = moe.route(logits, 2)
+    check_route(li.logits, None, 2, ids, w, err)
+
+
+def test_route_ties_signed_zero_and_masks(gpu):
+    import torch
+    rng = np.random.default_rng(0)
+    T, E, k = 200, 64, 6
+    lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, -0.0, 0.0).astype(np.float32)
+    ids, w, err = moe.route(torch.from_numpy(lg).to(gpu), k)
+    check_route(lg, None, k, ids, w, err)
+    mask = (rng.random(E) < 0.5).astype(np.uint8)
+    ids, w, err = moe.route(torch.from_numpy(lg).to(gpu), k, mask=torch.from_numpy(mask).to(gpu))
+    check_route(lg, mask, k, ids, w, err)
+    few = np.zeros(E, np.uint8)
+    few[[3, 17, 40]] = 1                       # fewer than k allowed experts
+    ids, w, err = moe.route(torch.from_numpy(lg).to(gpu), k, mask=torch.from_numpy(few).to(gpu))
+    check_route(lg, few, k, ids, w, err)
+    assert int(err.item()) == T
+
+
+@pytest.mark.parametrize("name,T", [("C1", 32), ("C2", 16384), ("C3", 32), ("C3", 4096)])
+def test_route_full_size(gpu, name, T):
+    c = CONFIGS[name]
+    li = make_layer(c, T, 0)
+    x, logits, soe, mask = device_inputs(li, gpu)
+    ids, w, err = moe.route(logits, c.k, mask=mask)
+    check_route(li.logits, li.mask, c.k, ids, w, err)
+
+
+def test_route_e1024_k32(gpu):
+    import torch
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((37, 1024)).astype(np.float32)
+    ids, w, err = moe.route(torch.from_numpy(lg).to(gpu), 32)
+    check_route(lg, None, 32, ids, w, err)
+
+
+# ---------------------------------------------------------------- align
+def _rand_ids(rng, T, k, E, skew=3.0):
+    p = rng.random(E) ** skew
+    p /= p.sum()
+    return np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,k,E,block_m", [(1, 8, 256, 16), (32, 8, 256, 16), (37, 3, 10, 64), (300, 8, 64, 32),
+                                           (1024, 8, 256, 256), (1025, 8, 256, 128), (4096, 10, 512, 128),
+                                           (16384, 8, 256, 128), (5000, 2, 1000, 16)])
+def test_align_matches_oracle(gpu, T, k, E, block_m):
+    import torch
+    rng = np.random.default_rng(T + E)
+    ids = _rand_ids(rng, T, k, E)
+    soe = rng.permutation(E).astype(np.int32)
+    soe[rng.random(E) < 0.05] = -1             # some experts not resident
+    _say(f"[align] T={T} k={k} E={E} bm={block_m} NP={T * k}")
+    al = moe.align(torch.from_numpy(ids).to(gpu), E, block_m, torch.from_numpy(soe).to(gpu))
+    ref = oracle.align(ids, E, block_m, soe)
+    check_align(al, ref, block_m)
+    al2 = moe.align(torch.from_numpy(ids).to(gpu), E, block_m, torch.from_numpy(soe).to(gpu))
+    n = ref["n_padded"]
+    assert torch.equal(al["sorted_pair"][:n], al2["sorted_pair"][:n])   # run-to-run identical
+
+
+def test_align_invalid_ids(gpu):
+    import torch
+    ids = np.array([[0, -1], [1, 0], [5, 2]], dtype=np.int32)    # -1 and 5 are outside [0, E)
+    soe = np.array([0, 1, 2], dtype=np.int32)
+    al = moe.align(torch.from_numpy(ids).to(gpu), 3, 16, torch.from_numpy(soe).to(gpu))
+    check_align(al, oracle.align(ids, 3, 16, soe), 16)
+    big = np.random.default_rng(1).integers(-2, 260, size=(2000, 8)).astype(np.int32)   # multi-block path
+    soe = np.arange(256, dtype=np.int32)
+    al = moe.align(torch.from_numpy(big).to(gpu), 256, 64, torch.from_numpy(soe).to(gpu))
+    check_align(al, oracle.align(big, 256, 64, soe), 64)
+
+
+# ---------------------------------------------------------------- expert FFN / whole layer
+@pytest.mark.parametrize("act_mode,block_m", [(0, 16), (0, 32), (0, 64), (1, 64), (1, 128)])
+def test_layer_c0(gpu, act_mode, block_m):
+    c = CONFIGS["C0"]
+    run_layer(make_layer(c, 16, 0), make_bank(c), gpu, block_m, act_mode)
+
+
+MID = Config("mid", 70, (300, 50), 256, 128, 16, 4, 1, 0.1, True, slots=0)
+MIX = Config("mix", 71, (200, 40), 256, 128, 16, 4, 1, 0.1, True, slots=0, int4_frac=0.4, resident_all_at=1)
+
+
+@pytest.mark.parametrize("cfg,T,act_mode,block_m", [(MID, 300, 1, 64), (MID, 300, 1, 128), (MID, 50, 0, 16),
+                                                    (MID, 50, 0, 64), (MID, 50, 1, 64), (MIX, 200, 1, 128),
+                                                    (MIX, 40, 0, 16), (MIX, 40, 0, 32), (MIX, 40, 1, 64)])
+def test_layer_mid_sizes(gpu, cfg, T, act_mode, block_m):
+    run_layer(make_layer(cfg, T, 0), make_bank(cfg), gpu, block_m, act_mode)
+
+
+def test_layer_single_token(gpu):
+    c = CONFIGS["C1"]
+    bank = make_bank(c)
+    run_layer(make_layer(c, 1, 3), bank, gpu, 16, 0)
+    run_layer(make_layer(c, 1, 3), bank, gpu, 64, 1)
+
+
+def test_nonresident_expert_contributes_zero(gpu):
+    c = CONFIGS["C0"]
+    li = make_layer(c, 16, 0)
+    ids, _, _ = oracle.route(li.logits, None, c.k)
+    li.slot_of_expert[int(ids[0, 0])] = -1
+    for act, bm in ((0, 16), (1, 64)):
+        out, ref = run_layer(li, make_bank(c), gpu, bm, act)
+        assert ref["err"] > 0
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_layer_c1_decode(gpu, T):
+    c = CONFIGS["C1"]
+    bank = make_bank(c)
+    li = make_layer(c, T, 7)
+    run_layer(li, bank, gpu, 16, 0)
+
+
+def test_layer_c3_masked_decode(gpu):
+    c = CONFIGS["C3"]
+    run_layer(make_layer(c, 32, 5), make_bank(c), gpu, 16, 0)
+
+
+def test_layer_c4_mixed_decode(gpu):
+    c = CONFIGS["C4"]
+    li = make_layer(c, 8, 2)
+    assert (li.slot_fmt == 1).any()
+    run_layer(li, make_bank(c), gpu, 16, 0)
+    run_layer(li, make_bank(c), gpu, 64, 1)
+
+
+@pytest.mark.parametrize("name,T,block_m", [("C2", 16384, 128), ("C4", 8192, 128), ("C3", 4096, 128)])
+def test_layer_batched_full_size_sampled(gpu, name, T, block_m):
+    c = CONFIGS[name]
+    bank = make_bank(c)
+    _say(f"[bank] {name}: generating {bank.n} experts")
+    bdev = bank_on_device(bank, gpu)
+    li = make_layer(c, T, 0)
+    sample = np.random.default_rng(T).choice(T, 48, replace=False)
+    run_layer(li, bank, gpu, block_m, 1, sample=sample, bank_dev=bdev)
+
+
+# ---------------------------------------------------------------- dequant
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_dequant_slot(gpu, fmt):
+    import torch
+    c = CONFIGS["C4"]
+    bank = make_bank(c)
+    li = make_layer(c, 8, 0)
+    pool = device_pool(li, bank, gpu)
+    s = int(np.nonzero(li.slot_fmt == fmt)[0][0])
+    w13, w2 = moe.dequant_slot(pool, s)
+    torch.cuda.synchronize()
+    R13, R2 = oracle.dequant_slot(bank.slot(li.slot_src[s], fmt), fmt, c.H, c.I)
+    for got, ref in ((w13, R13), (w2, R2)):
+        g = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -23)
