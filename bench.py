@@ -87,13 +87,14 @@ def main():
         cap = moe.align_capacity(T, k, E, bm)
         buf = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
                    w=torch.empty((T, k), dtype=torch.float32, device=dev),
-                   err=torch.zeros(1, dtype=torch.int32, device=dev),
+                   err=torch.zeros(2, dtype=torch.int32, device=dev),
                    al=dict(sorted_pair=torch.empty(cap, dtype=torch.int32, device=dev),
                            block_slot=torch.empty(cap // bm, dtype=torch.int32, device=dev),
                            counts=torch.empty(E, dtype=torch.int32, device=dev),
                            seg_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
                            n_padded=torch.empty(1, dtype=torch.int32, device=dev)),
-                   aws=torch.empty(max(1, moe.align_workspace_bytes(T, k, E, bm)), dtype=torch.uint8, device=dev),
+                   aws=torch.empty(max(1, moe.route_align_workspace_bytes(T, k, E, bm)), dtype=torch.uint8,
+                                   device=dev),
                    fws=torch.empty(max(1, moe.ffn_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
                                    device=dev),
                    out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
@@ -104,9 +105,8 @@ def main():
 
     def run_layer(entry, stream):
         li, pool, x, logits, soe, mask, b = entry
-        moe.route(logits, k, mask=mask, ids=b["ids"], w=b["w"], err=b["err"], stream=stream)
-        moe.align(b["ids"], E, bm, soe, out=b["al"], err=b["err"], ws=b["aws"] if b["aws"].numel() > 1 else None,
-                  stream=stream)
+        moe.route_align(logits, k, bm, soe, mask=mask, ids=b["ids"], w=b["w"], out=b["al"], err=b["err"],
+                        ws=b["aws"] if b["aws"].numel() > 1 else None, stream=stream)
         moe.expert_ffn(pool, x, k, E, b["w"], b["al"], bm, act, out=b["out"], ws=b["fws"], stream=stream)
 
     stream = torch.cuda.Stream()
@@ -177,15 +177,15 @@ def main():
     if act == moe.ACT_BF16:
         dom = "gemm1_stream"
         n, ms = prof[dom]
-        achieved = g1_bytes / n / (ms / n / 1e3) / 1e9
+        achieved = (g1_bytes / L) / (ms / n / 1e3) / 1e9        # bytes of one launch / its mean duration
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4))
         dtype = "bf16"
     else:
         dom = "gemm1_fp8"
         n, ms = prof[dom]
-        flops = 4 * T * k * H * I * L
-        achieved = flops / n / (ms / n / 1e3) / 1e12
+        flops = 4 * T * k * H * I                               # gate + up contraction of one launch
+        achieved = flops / (ms / n / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / FP8_PEAK_TFLOPS, 4))
         dtype = "fp8"

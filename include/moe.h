@@ -97,6 +97,17 @@ int moe_align(const int32_t* d_topk_ids, int T, int k, int E, int block_m,
               int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err,
               void* d_ws, size_t ws_bytes, void* stream);
 
+/* Route and align in one call: the same results as moe_route followed by
+ * moe_align on the same stream. d_err is i32[2]: [0] gets moe_route's count,
+ * [1] moe_align's (the -1 entries of short tokens count there too). The
+ * workspace is moe_align's. */
+size_t moe_route_align_workspace_bytes(int T, int k, int E, int block_m);
+int moe_route_align(const float* d_logits, const uint8_t* d_mask, int T, int E, int k, int block_m,
+                    const int32_t* d_slot_of_expert, int32_t* d_topk_ids, float* d_topk_w,
+                    int32_t* d_sorted_pair, int32_t* d_block_slot, int32_t* d_counts,
+                    int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err,
+                    void* d_ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- slot pool
  * [VEP] "hierarchical paging of expert weights": each MoE layer owns a pool
  * of VRAM slots, one expert per slot; the Table 1 set-up names the fused

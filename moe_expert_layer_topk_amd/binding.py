@@ -41,6 +41,8 @@ def _declare(lib):
         "moe_align_capacity": (c_int, [c_int, c_int, c_int, c_int]),
         "moe_align_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "moe_align": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P, P, c_size_t, P]),
+        "moe_route_align_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "moe_route_align": (c_int, [P, P, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "moe_slot_bytes": (c_size_t, [c_int, c_int, c_int]),
         "moe_slot_part_offset": (c_size_t, [c_int, c_int, c_int, c_int]),
         "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
@@ -143,11 +145,7 @@ def align(ids, E, block_m, slot_of_expert, out=None, err=None, ws=None, stream=N
     dev = ids.device
     cap = align_capacity(T, k, E, block_m)
     if out is None:
-        out = dict(sorted_pair=torch.empty(cap, dtype=torch.int32, device=dev),
-                   block_slot=torch.empty(cap // block_m, dtype=torch.int32, device=dev),
-                   counts=torch.empty(E, dtype=torch.int32, device=dev),
-                   seg_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
-                   n_padded=torch.empty(1, dtype=torch.int32, device=dev))
+        out = _align_out(T, k, E, block_m, dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
     need = align_workspace_bytes(T, k, E, block_m)
     if need and ws is None:
@@ -165,6 +163,51 @@ def align(ids, E, block_m, slot_of_expert, out=None, err=None, ws=None, stream=N
     out = dict(out)
     out["err"] = err
     return out
+
+
+def _align_out(T, k, E, block_m, dev):
+    import torch
+    cap = align_capacity(T, k, E, block_m)
+    return dict(sorted_pair=torch.empty(cap, dtype=torch.int32, device=dev),
+                block_slot=torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+                counts=torch.empty(E, dtype=torch.int32, device=dev),
+                seg_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                n_padded=torch.empty(1, dtype=torch.int32, device=dev))
+
+
+def route_align_workspace_bytes(T, k, E, block_m):
+    return int(lib().moe_route_align_workspace_bytes(T, k, E, block_m))
+
+
+def route_align(logits, k, block_m, slot_of_expert, mask=None, ids=None, w=None, out=None, err=None, ws=None,
+                stream=None):
+    """moe_route + moe_align in one call. Returns (ids, w, aligned dict); the
+    aligned dict's "err" is i32[2] (route count, align count)."""
+    import torch
+    T, E = logits.shape
+    dev = logits.device
+    cap = align_capacity(T, k, E, block_m)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    out = _align_out(T, k, E, block_m, dev) if out is None else out
+    err = torch.zeros(2, dtype=torch.int32, device=dev) if err is None else err
+    need = route_align_workspace_bytes(T, k, E, block_m)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_align(_ptr(logits, torch.float32, T * E, "logits"), _ptr(mask, torch.uint8, E, "mask"),
+                                 T, E, k, block_m, _ptr(slot_of_expert, torch.int32, E, "slot_of_expert"),
+                                 _ptr(ids, torch.int32, T * k, "ids"), _ptr(w, torch.float32, T * k, "w"),
+                                 _ptr(out["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                                 _ptr(out["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                                 _ptr(out["counts"], torch.int32, E, "counts"),
+                                 _ptr(out["seg_offset"], torch.int32, E + 1, "seg_offset"),
+                                 _ptr(out["n_padded"], torch.int32, 1, "n_padded"),
+                                 _ptr(err, torch.int32, 2, "err"),
+                                 _ptr(ws, torch.uint8, need, "ws") if need else None, c_size_t(need),
+                                 _stream(stream)))
+    out = dict(out)
+    out["err"] = err
+    return ids, w, out
 
 
 # ---------------------------------------------------------------- slot pool
@@ -246,10 +289,17 @@ def profile_read():
 
 
 # ---------------------------------------------------------------- whole layer
-def layer(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, stream=None):
-    """route -> align -> expert FFN on one stream; returns (out, route, align)."""
+def layer(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, stream=None, fused=False):
+    """route -> align -> expert FFN on one stream; returns (out, route, align).
+    fused=True routes and aligns through moe_route_align (then the route
+    error count is aligned["err"][0:1] and align's is aligned["err"][1:2])."""
     E = logits.shape[1]
-    ids, w, rerr = route(logits, k, mask=mask, stream=stream)
-    al = align(ids, E, block_m, slot_of_expert, stream=stream)
+    if fused:
+        ids, w, al = route_align(logits, k, block_m, slot_of_expert, mask=mask, stream=stream)
+        rerr = al["err"][0:1]
+        al["err"] = al["err"][1:2]
+    else:
+        ids, w, rerr = route(logits, k, mask=mask, stream=stream)
+        al = align(ids, E, block_m, slot_of_expert, stream=stream)
     out = expert_ffn(pool, x, k, E, w, al, block_m, act_mode, stream=stream)
     return out, (ids, w, rerr), al

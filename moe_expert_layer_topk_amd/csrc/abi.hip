@@ -48,7 +48,7 @@ void slot_parts(int H, int I, int fmt, size_t off[4], size_t* total) {
 }
 
 bool pool_args(const moe_slot_pool* pool, moe::PoolArgs* pa) {
-    if (!pool || !pool->d_base || !pool->d_slot_fmt || pool->n_slots < 1) return false;
+    if (!pool || !pool->d_base || !pool->d_slot_fmt || pool->n_slots < 1 || pool->n_slots > MOE_MAX_SLOTS) return false;
     const int H = pool->hidden, I = pool->inter;
     if (H < 128 || H % 128 || I < 64 || I % 64) return false;
     size_t fp8_bytes, int4_bytes = 0;
@@ -65,6 +65,7 @@ bool pool_args(const moe_slot_pool* pool, moe::PoolArgs* pa) {
     pa->base = pool->d_base;
     pa->stride = pool->slot_bytes;
     pa->fmt = pool->d_slot_fmt;
+    pa->n_slots = pool->n_slots;
     pa->hidden = H;
     pa->inter = I;
     return true;
@@ -123,8 +124,31 @@ int moe_align(const int32_t* d_topk_ids, int T, int k, int E, int block_m, const
     size_t need = moe::align_workspace_bytes(T * k, E);
     if (need && (!d_ws || ws_bytes < need)) return MOE_EINVAL;
     clear_stale_error();
-    return hip_status(moe::launch_align(d_topk_ids, T * k, E, block_m, d_slot_of_expert, d_sorted_pair, d_block_slot,
+    return hip_status(moe::launch_align(d_topk_ids, T, k, E, block_m, d_slot_of_expert, d_sorted_pair, d_block_slot,
                                         d_counts, d_seg_offset, d_n_padded, d_err, d_ws, (hipStream_t)stream));
+}
+
+int moe_route_align(const float* d_logits, const uint8_t* d_mask, int T, int E, int k, int block_m,
+                    const int32_t* d_slot_of_expert, int32_t* d_topk_ids, float* d_topk_w, int32_t* d_sorted_pair,
+                    int32_t* d_block_slot, int32_t* d_counts, int32_t* d_seg_offset, int32_t* d_n_padded,
+                    int32_t* d_err, void* d_ws, size_t ws_bytes, void* stream) {
+    if (!d_logits || !d_slot_of_expert || !d_topk_ids || !d_topk_w || !d_sorted_pair || !d_block_slot || !d_counts ||
+        !d_seg_offset || !d_n_padded || !d_err)
+        return MOE_EINVAL;
+    if (T < 1 || E < 1 || E > MOE_MAX_E || k < 1 || k > E || k > MOE_MAX_K || !valid_block_m(block_m))
+        return MOE_EINVAL;
+    if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
+    const size_t need = moe_route_align_workspace_bytes(T, k, E, block_m);
+    if (need && (!d_ws || ws_bytes < need)) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_route_align(d_logits, d_mask, T, E, k, block_m, d_slot_of_expert, d_topk_ids,
+                                              d_topk_w, d_sorted_pair, d_block_slot, d_counts, d_seg_offset,
+                                              d_n_padded, d_err, d_ws, (hipStream_t)stream));
+}
+
+size_t moe_route_align_workspace_bytes(int T, int k, int E, int block_m) {
+    if (T < 1 || k < 1 || E < 1 || E > MOE_MAX_E || !valid_block_m(block_m)) return 0;
+    return moe::align_workspace_bytes(T * k, E);
 }
 
 size_t moe_slot_bytes(int hidden, int inter, int fmt) {
@@ -146,7 +170,7 @@ size_t moe_slot_part_offset(int hidden, int inter, int fmt, int part) {
 size_t moe_ffn_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode) {
     if (T < 1 || k < 1 || E < 1 || !valid_block_m(block_m)) return 0;
     const int cap = capacity(T, k, E, block_m);
-    if (act_mode == MOE_ACT_BF16) return moe::stream_workspace_bytes(cap, inter);
+    if (act_mode == MOE_ACT_BF16) return moe::stream_workspace_bytes(T, k, hidden, inter, cap);
     if (act_mode == MOE_ACT_FP8_G128_POW2) return moe::grouped_workspace_bytes(T, k, hidden, inter, cap);
     return 0;
 }
@@ -163,7 +187,7 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
     if (act_mode == MOE_ACT_BF16) {
         if (block_m != 16 && block_m != 32 && block_m != 64) return MOE_EINVAL;
         if (T > moe::stream_max_tokens()) return MOE_EINVAL;
-        if (ws_bytes < moe::stream_workspace_bytes(cap, pa.inter)) return MOE_EINVAL;
+        if (ws_bytes < moe::stream_workspace_bytes(T, k, pa.hidden, pa.inter, cap)) return MOE_EINVAL;
         clear_stale_error();
     return hip_status(moe::launch_ffn_stream(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
                                                  cap, block_m, d_out, d_ws, (hipStream_t)stream));

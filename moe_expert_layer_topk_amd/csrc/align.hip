@@ -197,17 +197,82 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scatter_kernel(const int3
     scatter_pairs(ids, p0, p1, E, s_run, s_wcnt, sorted_pair);
 }
 
+// Decode-sized batches (T <= 64): the stable rank of pair (t, j) inside
+// expert e's segment is the number of earlier tokens that chose e, read off a
+// per-expert 64-bit token mask built with LDS atomics. One workgroup, no
+// counting rounds; ids and the slot table are loaded in one round trip.
+constexpr int MASK_MAX_T = 64;
+
+__global__ void __launch_bounds__(ALIGN_THREADS) align_mask_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int block_m, const int32_t* __restrict__ slot_of_expert,
+    int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
+    int32_t* err) {
+    __shared__ unsigned long long s_tok[MOE_MAX_E];   // bit t set: token t chose the expert
+    __shared__ int s_cnt[MOE_MAX_E];
+    __shared__ int s_off[MOE_MAX_E];
+    __shared__ int s_tmp[2 * ALIGN_WAVES];
+    __shared__ uint8_t s_wcnt[ALIGN_WAVES * MOE_MAX_E];
+    const int tid = threadIdx.x;
+    const int NP = T * k;
+    const int my_id = tid < NP ? ids[tid] : -1;           // NP <= ALIGN_THREADS is checked by the host
+    for (int i = tid; i < E; i += ALIGN_THREADS) {
+        s_tok[i] = 0ull;
+        s_cnt[i] = 0;
+    }
+    __syncthreads();
+    const bool valid = my_id >= 0 && my_id < E;
+    if (valid) {
+        atomicOr(&s_tok[my_id], 1ull << (tid / k));
+        atomicAdd(&s_cnt[my_id], 1);
+    }
+    const uint64_t bad = __ballot(tid < NP && !valid);
+    if (lane_id() == 0 && bad) atomicAdd(err, (int)__popcll(bad));
+    __syncthreads();
+    // a token listing one expert twice breaks the mask ranks: take the counting path then
+    const bool dup = __syncthreads_or(tid < E && s_cnt[tid] != (int)__popcll(s_tok[tid]));
+    segments_from_counts(s_cnt, s_off, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
+                         block_slot, sorted_pair, err);
+    if (dup) {
+        scatter_pairs(ids, 0, NP, E, s_off, s_wcnt, sorted_pair);
+        return;
+    }
+    if (valid) {
+        const int tt = tid / k;
+        const unsigned long long before = tt == 0 ? 0ull : (s_tok[my_id] & (~0ull >> (64 - tt)));
+        sorted_pair[s_off[my_id] + (int)__popcll(before)] = tid;
+    }
+}
+
+int route_align_fused_max_pairs() { return MASK_MAX_T; }
+
+hipError_t launch_route_align(const float* logits, const uint8_t* mask, int T, int E, int k, int block_m,
+                              const int32_t* slot_of_expert, int32_t* ids, float* w, int32_t* sorted_pair,
+                              int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
+                              int32_t* err, void* ws, hipStream_t stream) {
+    // the route error count lands in err[0]; align counts the -1 entries of short tokens in err[1]
+    hipError_t e = launch_route(logits, mask, T, E, k, ids, w, err, stream);
+    if (e != hipSuccess) return e;
+    return launch_align(ids, T, k, E, block_m, slot_of_expert, sorted_pair, block_slot, counts, seg_offset,
+                        n_padded, err + 1, ws, stream);
+}
+
 int align_single_max_pairs() { return 8192; }
 
 size_t align_workspace_bytes(int NP, int E) {
-    if (NP <= align_single_max_pairs()) return 0;
+    if (NP <= align_single_max_pairs()) return 0;   // (the token-mask path needs none either)
     size_t chunks = (size_t)(NP + ALIGN_CHUNK - 1) / ALIGN_CHUNK;
     return chunks * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_align(const int32_t* ids, int NP, int E, int block_m, const int32_t* slot_of_expert,
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, const int32_t* slot_of_expert,
                         int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset,
                         int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream) {
+    const int NP = T * k;
+    if (T <= MASK_MAX_T && NP <= ALIGN_THREADS) {
+        MOE_LAUNCH(K_ALIGN_SINGLE, stream, align_mask_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, ids, T, k, E,
+                   block_m, slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+        return hipGetLastError();
+    }
     if (NP <= align_single_max_pairs()) {
         MOE_LAUNCH(K_ALIGN_SINGLE, stream, align_single_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, ids, NP, E, block_m,
                            slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);

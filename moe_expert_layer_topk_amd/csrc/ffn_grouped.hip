@@ -383,29 +383,6 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
     }
 }
 
-// ------------------------------------------------------------ combine
-// One workgroup per token; each thread sums 8 columns over the k pairs.
-__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ ybuf, const float* __restrict__ topk_w,
-                                                     int T, int k, int H, uint16_t* __restrict__ out) {
-    const int t = blockIdx.x;
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-        float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) {
-            if (topk_w[(size_t)t * k + j] == 0.f) continue;   // missing route entry: row never written
-            i32x4 v = *(const i32x4*)(ybuf + ((size_t)t * k + j) * H + c);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                s[2 * d] += bf16_to_f32((uint16_t)((uint32_t)v[d] & 0xFFFF));
-                s[2 * d + 1] += bf16_to_f32((uint16_t)((uint32_t)v[d] >> 16));
-            }
-        }
-        i32x4 o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = (int)((uint32_t)f32_to_bf16(s[2 * d]) | ((uint32_t)f32_to_bf16(s[2 * d + 1]) << 16));
-        *(i32x4*)(out + (size_t)t * H + c) = o;
-    }
-}
-
 // ------------------------------------------------------------ host side
 static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -458,8 +435,9 @@ static hipError_t launch_grouped_bm(const GPool& gp, const GroupedWs& w, const u
     dim3 g2(H / 128, cap / BM);
     MOE_LAUNCH(K_GEMM2_FP8, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k, topk_w, sorted_pair,
                        block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf);
-    MOE_LAUNCH(K_COMBINE, stream, combine_kernel, dim3(T), dim3(256), 0, stream, w.ybuf, topk_w, T, k, H, out);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_combine_bf16(w.ybuf, topk_w, T, k, H, out, stream);
 }
 
 hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,

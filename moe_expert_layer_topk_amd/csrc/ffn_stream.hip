@@ -3,18 +3,19 @@
 // vllm-expert-pager article (rand.pepabo.com), Table 1 set-up: each expert
 // has w13 (gate and up fused) and w2 (down); "hierarchical paging" section:
 // they are read from the expert's VRAM slot. At decode sizes the layer is
-// bound by reading those slots once from HBM, so both kernels stream weight
-// rows with 16-byte loads spread over the whole chip and feed them, converted
-// to bf16 (exact for e4m3 codes and for int4 q - zero), to bf16 matrix cores
-// against the few token rows of each expert.
+// bound by reading those slots once from HBM, so both kernels cut the routed
+// experts' weights into many small units spread over the whole chip, issue
+// every 16-byte load of a unit before using any (one memory round trip per
+// unit), and feed the rows, converted to bf16 (exact for e4m3 codes and for
+// int4 q - zero), to bf16 matrix cores against the few token rows of each
+// expert.
 //
-// Kernel 1 (gate/up): unit = (block of pairs, 16 rows of inter). Each of the
-//   4 waves takes a quarter of the K = hidden groups; partial sums meet in
-//   LDS; the epilogue applies row scales, silu(gate) * up, and stores h (bf16).
-// Kernel 2 (down + combine): each workgroup owns 16 output columns of every
-//   token. Its 8 waves walk the blocks, multiply W2 rows by h and add
-//   w[t][j] * y into per-wave LDS accumulators, which are summed in a fixed
-//   order and rounded once to bf16: no atomics, deterministic.
+// gemm1 (gate/up): unit = (block of pairs, 16 rows of inter). The 4 waves of
+//   a workgroup split K = hidden by 128-wide groups; partial sums meet in
+//   LDS; the epilogue applies row scales, silu(gate) * up and stores h (bf16).
+// gemm2 (down): unit = (block of pairs, 64 rows of hidden); each wave owns 16
+//   rows, multiplies them by h and writes w[t][j] * y for each pair (fp32).
+// combine: out[t] = sum_j ybuf[t*k + j], fixed order, rounded once to bf16.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l = m + 16 q): A row m and
 // B column m hold K positions 8q..8q+7; C lane l holds rows 4q..4q+3 of
@@ -33,10 +34,7 @@ struct SlotView {
     size_t off[2][4];      // part offsets per format
 };
 
-// 16 K values of row `row` at K offset k0 (multiple of 16) as two bf16x8
-// operands. FP8 rows: codes. INT4 rows: q - zero of the row's K group.
-__device__ __forceinline__ void load_w16_fp8(const uint8_t* rowp, int k0, bf16x8& s0, bf16x8& s1) {
-    i32x4 v = *(const i32x4*)(rowp + k0);
+__device__ __forceinline__ void fp8x16_to_bf16(const i32x4& v, bf16x8& s0, bf16x8& s1) {
     uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
     e4m3x4_to_bf16x4((uint32_t)v[0], a0, a1);
     e4m3x4_to_bf16x4((uint32_t)v[1], a2, a3);
@@ -52,32 +50,26 @@ __device__ __forceinline__ uint32_t two_bf16(float a, float b) {
     return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-__device__ __forceinline__ void load_w16_int4(const uint8_t* rowp_packed, int k0, float zero, bf16x8& s0,
-                                              bf16x8& s1) {
-    uint2 v = *(const uint2*)(rowp_packed + k0 / 2);
+// 16 int4 values (8 bytes) -> q - zero as two bf16x8 operands
+__device__ __forceinline__ void int4x16_to_bf16(uint2 v, float zero, bf16x8& s0, bf16x8& s1) {
     uint32_t w[2] = {v.x, v.y};
     uint32_t o[8];
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             uint32_t byte = (w[d] >> (8 * j)) & 0xFFu;
-            float lo = (float)(byte & 0xFu) - zero;
-            float hi = (float)(byte >> 4) - zero;
-            o[d * 4 + j] = two_bf16(lo, hi);
+            o[d * 4 + j] = two_bf16((float)(byte & 0xFu) - zero, (float)(byte >> 4) - zero);
         }
-    }
     i32x4 x0 = {(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     i32x4 x1 = {(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
     s0 = __builtin_bit_cast(bf16x8, x0);
     s1 = __builtin_bit_cast(bf16x8, x1);
 }
 
-// 16 bf16 of a token row at K offset k0 as two operands (no conversion)
-__device__ __forceinline__ void load_x16(const uint16_t* xrow, int k0, bf16x8& s0, bf16x8& s1) {
-    const i32x4* p = (const i32x4*)(xrow + k0);
-    s0 = __builtin_bit_cast(bf16x8, p[0]);
-    s1 = __builtin_bit_cast(bf16x8, p[1]);
+__device__ __forceinline__ void split_bf16(const i32x4& lo, const i32x4& hi, bf16x8& s0, bf16x8& s1) {
+    s0 = __builtin_bit_cast(bf16x8, lo);
+    s1 = __builtin_bit_cast(bf16x8, hi);
 }
 
 __device__ __forceinline__ float2 half2_at(const uint8_t* p) {
@@ -85,54 +77,97 @@ __device__ __forceinline__ float2 half2_at(const uint8_t* p) {
     return make_float2((float)h[0], (float)h[1]);
 }
 
-constexpr int G1_THREADS = 256;
-constexpr int G1_WAVES = 4;
-constexpr int ROWS = 16;    // inter rows (gate and up each) per unit
+constexpr int G_THREADS = 256;
+constexpr int G_WAVES = 4;
+constexpr int ROWS = 16;      // inter rows (gate and up each) per gemm1 unit
+constexpr int G1_MAXG = 4;    // K groups per wave issued together
+constexpr int G2_COLS = 64;   // hidden rows per gemm2 unit
+constexpr int G2_MAXC = 8;    // 64-wide K chunks per wave issued together
+constexpr int STREAM_MAX_T = 64;
 
+// ------------------------------------------------------------ gemm1
+// One unit per workgroup. Round trip 1: n_padded, the block's slot and pair
+// list, and the pool's format tags (into LDS). Round trip 2: every weight
+// row chunk, token row chunk and row scale of the unit at once.
 template <int BM>
-__global__ void __launch_bounds__(G1_THREADS) gemm1_stream_kernel(
-    SlotView pool, const uint16_t* __restrict__ x, int NP, int k, const int32_t* __restrict__ sorted_pair,
+__global__ void __launch_bounds__(G_THREADS) gemm1_stream_kernel(
+    SlotView pool, int n_slots, const uint16_t* __restrict__ x, int NP, int k, const int32_t* __restrict__ sorted_pair,
     const int32_t* __restrict__ block_slot, const int32_t* __restrict__ n_padded, int H, int I,
     uint16_t* __restrict__ hbuf) {
     constexpr int NT = BM / 16;
-    __shared__ f32x4 s_red[G1_WAVES][NT][2][MOE_WAVE];
+    __shared__ f32x4 s_red[G_WAVES][NT][2][MOE_WAVE];
+    __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
     const int m = lane & 15, q = lane >> 4;
     const int ntile = I / ROWS;
-    const int nblocks = *n_padded / BM;
-    const int n_units = nblocks * ntile;
-    const int groups = H / MOE_INT4_G;
-    for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-        const int b = u / ntile, i0 = (u % ntile) * ROWS;
-        const int slot = block_slot[b];
-        if (slot < 0) continue;                       // uniform over the workgroup
-        const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-        const int fmt = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
-        const uint16_t* xr[NT];
-        int pos[NT];
+    const int u = blockIdx.x;
+    const int b = u / ntile, i0 = (u % ntile) * ROWS;
+    const int groups = H / 128;
+    // ---- round trip 1 (all inside the arrays: b < capacity / BM)
+    const int npad = *n_padded;
+    const int slot = block_slot[b];
+    int pr[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            pos[nt] = b * BM + nt * 16 + m;
-            int p = sorted_pair[pos[nt]];
-            xr[nt] = x + (size_t)(p < NP ? p / k : 0) * H;
-        }
-        f32x4 acc_g[NT], acc_u[NT];
+    for (int nt = 0; nt < NT; ++nt) pr[nt] = sorted_pair[b * BM + nt * 16 + m];
+    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+    __syncthreads();
+    if (b >= npad / BM || slot < 0) return;           // uniform over the workgroup
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    const int fmt = (s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+    const uint16_t* xr[NT];
+    bool pv[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) { acc_g[nt] = f32x4{0, 0, 0, 0}; acc_u[nt] = f32x4{0, 0, 0, 0}; }
-        if (fmt == 0) {
-            const uint8_t* wg = sb + (size_t)(i0 + m) * H;
-            const uint8_t* wu = sb + (size_t)(I + i0 + m) * H;
-            for (int g = wv; g < groups; g += G1_WAVES) {
+    for (int nt = 0; nt < NT; ++nt) {
+        pv[nt] = pr[nt] < NP;
+        xr[nt] = x + (size_t)(pv[nt] ? pr[nt] / k : 0) * H;
+    }
+    f32x4 acc_g[NT], acc_u[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) { acc_g[nt] = f32x4{0, 0, 0, 0}; acc_u[nt] = f32x4{0, 0, 0, 0}; }
+    f32x4 sg4 = {1, 1, 1, 1}, su4 = {1, 1, 1, 1};
+    if (fmt == 0) {
+        // ---- round trip 2
+        const float* s13 = (const float*)(sb + pool.off[0][1]);
+        sg4 = *(const f32x4*)(s13 + i0 + 4 * q);
+        su4 = *(const f32x4*)(s13 + I + i0 + 4 * q);
+        const uint8_t* wg = sb + (size_t)(i0 + m) * H;
+        const uint8_t* wu = sb + (size_t)(I + i0 + m) * H;
+        for (int g0 = wv; g0 < groups; g0 += G_WAVES * G1_MAXG) {
+            i32x4 rg[G1_MAXG][2], ru[G1_MAXG][2], rx[G1_MAXG][2][NT][2];
+#pragma unroll
+            for (int j = 0; j < G1_MAXG; ++j) {
+                const int g = g0 + j * G_WAVES;
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const int k0 = g * 128 + c * 64 + q * 16;
+                    if (g < groups) {
+                        rg[j][c] = *(const i32x4*)(wg + k0);
+                        ru[j][c] = *(const i32x4*)(wu + k0);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        if (g < groups && pv[nt]) {
+                            rx[j][c][nt][0] = *(const i32x4*)(xr[nt] + k0);
+                            rx[j][c][nt][1] = *(const i32x4*)(xr[nt] + k0 + 8);
+                        } else {
+                            rx[j][c][nt][0] = i32x4{0, 0, 0, 0};
+                            rx[j][c][nt][1] = i32x4{0, 0, 0, 0};
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < G1_MAXG; ++j) {
+                if (g0 + j * G_WAVES >= groups) break;   // uniform over the wave
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
                     bf16x8 ga0, ga1, ua0, ua1;
-                    load_w16_fp8(wg, k0, ga0, ga1);
-                    load_w16_fp8(wu, k0, ua0, ua1);
+                    fp8x16_to_bf16(rg[j][c], ga0, ga1);
+                    fp8x16_to_bf16(ru[j][c], ua0, ua1);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         bf16x8 xb0, xb1;
-                        load_x16(xr[nt], k0, xb0, xb1);
+                        split_bf16(rx[j][c][nt][0], rx[j][c][nt][1], xb0, xb1);
                         acc_g[nt] = mfma_bf16_16x16x32(ga0, xb0, acc_g[nt]);
                         acc_g[nt] = mfma_bf16_16x16x32(ga1, xb1, acc_g[nt]);
                         acc_u[nt] = mfma_bf16_16x16x32(ua0, xb0, acc_u[nt]);
@@ -140,165 +175,318 @@ __global__ void __launch_bounds__(G1_THREADS) gemm1_stream_kernel(
                     }
                 }
             }
-        } else {
-            const uint8_t* wg = sb + (size_t)(i0 + m) * (H / 2);
-            const uint8_t* wu = sb + (size_t)(I + i0 + m) * (H / 2);
-            const uint8_t* sz = sb + pool.off[1][1];
-            for (int g = wv; g < groups; g += G1_WAVES) {
-                const float zg = half2_at(sz + ((size_t)(i0 + m) * groups + g) * 4).y;
-                const float zu = half2_at(sz + ((size_t)(I + i0 + m) * groups + g) * 4).y;
-                f32x4 tg[NT], tu[NT];
+        }
+    } else {
+        const uint8_t* wg = sb + (size_t)(i0 + m) * (H / 2);
+        const uint8_t* wu = sb + (size_t)(I + i0 + m) * (H / 2);
+        const uint8_t* sz = sb + pool.off[1][1];
+        for (int g = wv; g < groups; g += G_WAVES) {
+            const float zg = half2_at(sz + ((size_t)(i0 + m) * groups + g) * 4).y;
+            const float zu = half2_at(sz + ((size_t)(I + i0 + m) * groups + g) * 4).y;
+            uint2 rg[2], ru[2];
+            i32x4 rx[2][NT][2];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) { tg[nt] = f32x4{0, 0, 0, 0}; tu[nt] = f32x4{0, 0, 0, 0}; }
+            for (int c = 0; c < 2; ++c) {
+                const int k0 = g * 128 + c * 64 + q * 16;
+                rg[c] = *(const uint2*)(wg + k0 / 2);
+                ru[c] = *(const uint2*)(wu + k0 / 2);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int k0 = g * 128 + c * 64 + q * 16;
-                    bf16x8 ga0, ga1, ua0, ua1;
-                    load_w16_int4(wg, k0, zg, ga0, ga1);
-                    load_w16_int4(wu, k0, zu, ua0, ua1);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        bf16x8 xb0, xb1;
-                        load_x16(xr[nt], k0, xb0, xb1);
-                        tg[nt] = mfma_bf16_16x16x32(ga0, xb0, tg[nt]);
-                        tg[nt] = mfma_bf16_16x16x32(ga1, xb1, tg[nt]);
-                        tu[nt] = mfma_bf16_16x16x32(ua0, xb0, tu[nt]);
-                        tu[nt] = mfma_bf16_16x16x32(ua1, xb1, tu[nt]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    if (pv[nt]) {
+                        rx[c][nt][0] = *(const i32x4*)(xr[nt] + k0);
+                        rx[c][nt][1] = *(const i32x4*)(xr[nt] + k0 + 8);
+                    } else {
+                        rx[c][nt][0] = i32x4{0, 0, 0, 0};
+                        rx[c][nt][1] = i32x4{0, 0, 0, 0};
                     }
                 }
-                // group scales of the output rows this lane holds (rows 4q..4q+3)
+            }
+            f32x4 tg[NT], tu[NT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float sg = half2_at(sz + ((size_t)(i0 + 4 * q + i) * groups + g) * 4).x;
-                    const float su = half2_at(sz + ((size_t)(I + i0 + 4 * q + i) * groups + g) * 4).x;
+            for (int nt = 0; nt < NT; ++nt) { tg[nt] = f32x4{0, 0, 0, 0}; tu[nt] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        acc_g[nt][i] += sg * tg[nt][i];
-                        acc_u[nt][i] += su * tu[nt][i];
-                    }
+            for (int c = 0; c < 2; ++c) {
+                bf16x8 ga0, ga1, ua0, ua1;
+                int4x16_to_bf16(rg[c], zg, ga0, ga1);
+                int4x16_to_bf16(ru[c], zu, ua0, ua1);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    bf16x8 xb0, xb1;
+                    split_bf16(rx[c][nt][0], rx[c][nt][1], xb0, xb1);
+                    tg[nt] = mfma_bf16_16x16x32(ga0, xb0, tg[nt]);
+                    tg[nt] = mfma_bf16_16x16x32(ga1, xb1, tg[nt]);
+                    tu[nt] = mfma_bf16_16x16x32(ua0, xb0, tu[nt]);
+                    tu[nt] = mfma_bf16_16x16x32(ua1, xb1, tu[nt]);
+                }
+            }
+            // group scales of the output rows this lane holds (rows 4q..4q+3)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sg = half2_at(sz + ((size_t)(i0 + 4 * q + i) * groups + g) * 4).x;
+                const float su = half2_at(sz + ((size_t)(I + i0 + 4 * q + i) * groups + g) * 4).x;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    acc_g[nt][i] += sg * tg[nt][i];
+                    acc_u[nt][i] += su * tu[nt][i];
                 }
             }
         }
+    }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) { s_red[wv][nt][0][lane] = acc_g[nt]; s_red[wv][nt][1][lane] = acc_u[nt]; }
-        __syncthreads();
-        if (wv < NT) {                       // wave wv finishes pair tile nt = wv
-            const int nt = wv;
-            f32x4 g = s_red[0][nt][0][lane], up = s_red[0][nt][1][lane];
+    for (int nt = 0; nt < NT; ++nt) { s_red[wv][nt][0][lane] = acc_g[nt]; s_red[wv][nt][1][lane] = acc_u[nt]; }
+    __syncthreads();
+    if (wv < NT) {                       // wave wv finishes pair tile nt = wv
+        const int nt = wv;
+        f32x4 g = s_red[0][nt][0][lane], up = s_red[0][nt][1][lane];
 #pragma unroll
-            for (int w2 = 1; w2 < G1_WAVES; ++w2) {
-                g += s_red[w2][nt][0][lane];
-                up += s_red[w2][nt][1][lane];
-            }
-            int p = sorted_pair[b * BM + nt * 16 + m];
-            if (p < NP) {
-                uint32_t packed[2];
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    float hv[2];
-#pragma unroll
-                    for (int d = 0; d < 2; ++d) {
-                        const int r = i0 + 4 * q + i + d;
-                        float gs = g[i + d], us = up[i + d];
-                        if (fmt == 0) {
-                            gs *= ((const float*)(sb + pool.off[0][1]))[r];
-                            us *= ((const float*)(sb + pool.off[0][1]))[I + r];
-                        }
-                        hv[d] = silu(gs) * us;
-                    }
-                    packed[i / 2] = two_bf16(hv[0], hv[1]);
-                }
-                *(uint2*)(hbuf + (size_t)(b * BM + nt * 16 + m) * I + i0 + 4 * q) = make_uint2(packed[0], packed[1]);
-            }
+        for (int w2 = 1; w2 < G_WAVES; ++w2) {
+            g += s_red[w2][nt][0][lane];
+            up += s_red[w2][nt][1][lane];
         }
-        __syncthreads();
+        if (pr[nt] < NP) {
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = silu(g[i] * sg4[i]) * (up[i] * su4[i]);
+            *(uint2*)(hbuf + (size_t)(b * BM + nt * 16 + m) * I + i0 + 4 * q) =
+                make_uint2(two_bf16(hv[0], hv[1]), two_bf16(hv[2], hv[3]));
+        }
     }
 }
 
-constexpr int G2_THREADS = 512;
-constexpr int G2_WAVES = 8;
-constexpr int STREAM_MAX_T = 64;
-
+// ------------------------------------------------------------ gemm2
+// One unit per workgroup: (block, 64 hidden rows); wave w owns 16 rows.
+// Round trip 1 as in gemm1; round trip 2: W2 row chunks, h rows of the
+// block's valid pairs, row scales and route weights.
 template <int BM>
-__global__ void __launch_bounds__(G2_THREADS) gemm2_stream_kernel(
-    SlotView pool, int T, int NP, int k, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_pair,
-    const int32_t* __restrict__ block_slot, const int32_t* __restrict__ n_padded, int H, int I,
-    const uint16_t* __restrict__ hbuf, uint16_t* __restrict__ out) {
+__global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
+    SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
+    const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf) {
     constexpr int NT = BM / 16;
-    __shared__ float s_acc[G2_WAVES][STREAM_MAX_T][16];
+    __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
     const int m = lane & 15, q = lane >> 4;
-    const int n0 = blockIdx.x * 16;
-    for (int i = threadIdx.x; i < G2_WAVES * STREAM_MAX_T * 16; i += G2_THREADS) (&s_acc[0][0][0])[i] = 0.f;
-    __syncthreads();
-    const int nblocks = *n_padded / BM;
+    const int ntile = H / G2_COLS;
+    const int u = blockIdx.x;
+    const int b = u / ntile;
+    const int n0 = (u % ntile) * G2_COLS + wv * 16;   // this wave's 16 rows
     const int chunks = I / 64;
-    const int groups = (I + MOE_INT4_G - 1) / MOE_INT4_G;
-    for (int b = wv; b < nblocks; b += G2_WAVES) {
-        const int slot = block_slot[b];
-        if (slot < 0) continue;                       // uniform over the wave
-        const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-        const int fmt = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+    const int groups = I / MOE_INT4_G;
+    // ---- round trip 1
+    const int npad = *n_padded;
+    const int slot = block_slot[b];
+    int pr[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int pos = b * BM + nt * 16 + m;
-            const int p = sorted_pair[pos];
-            const uint16_t* hr = hbuf + (size_t)pos * I;
-            f32x4 acc = {0, 0, 0, 0};
-            if (fmt == 0) {
-                const uint8_t* wr = sb + pool.off[0][2] + (size_t)(n0 + m) * I;
-                for (int c = 0; c < chunks; ++c) {
-                    const int k0 = c * 64 + q * 16;
-                    bf16x8 a0, a1, h0, h1;
-                    load_w16_fp8(wr, k0, a0, a1);
-                    load_x16(hr, k0, h0, h1);
-                    acc = mfma_bf16_16x16x32(a0, h0, acc);
-                    acc = mfma_bf16_16x16x32(a1, h1, acc);
-                }
-                const float* s2 = (const float*)(sb + pool.off[0][3]);
+    for (int nt = 0; nt < NT; ++nt) pr[nt] = sorted_pair[b * BM + nt * 16 + m];
+    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+    __syncthreads();
+    if (b >= npad / BM) return;                       // uniform over the workgroup
+    bool pv[NT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= s2[n0 + 4 * q + i];
-            } else {
-                const uint8_t* wr = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2);
-                const uint8_t* sz = sb + pool.off[1][3];
-                for (int g = 0; g < groups; ++g) {
-                    const float z = half2_at(sz + ((size_t)(n0 + m) * groups + g) * 4).y;
-                    f32x4 t4 = {0, 0, 0, 0};
+    for (int nt = 0; nt < NT; ++nt) pv[nt] = pr[nt] < NP;
+    if (slot < 0) {                                   // non-resident expert: its pairs add zero
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int k0 = g * 128 + c * 64 + q * 16;
-                        bf16x8 a0, a1, h0, h1;
-                        load_w16_int4(wr, k0, z, a0, a1);
-                        load_x16(hr, k0, h0, h1);
-                        t4 = mfma_bf16_16x16x32(a0, h0, t4);
-                        t4 = mfma_bf16_16x16x32(a1, h1, t4);
+        for (int nt = 0; nt < NT; ++nt)
+            if (pv[nt]) *(f32x4*)(ybuf + (size_t)pr[nt] * H + n0 + 4 * q) = f32x4{0, 0, 0, 0};
+        return;
+    }
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    const int fmt = (s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+    float wt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wt[nt] = pv[nt] ? topk_w[pr[nt]] : 0.f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+    if (fmt == 0) {
+        const f32x4 s2 = *(const f32x4*)((const float*)(sb + pool.off[0][3]) + n0 + 4 * q);
+        const uint8_t* wr = sb + pool.off[0][2] + (size_t)(n0 + m) * I;
+        for (int c0 = 0; c0 < chunks; c0 += G2_MAXC) {
+            i32x4 rw[G2_MAXC], rh[G2_MAXC][NT][2];
+#pragma unroll
+            for (int j = 0; j < G2_MAXC; ++j) {
+                const int c = c0 + j;
+                const int k0 = c * 64 + q * 16;
+                if (c < chunks) rw[j] = *(const i32x4*)(wr + k0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint16_t* hr = hbuf + (size_t)(b * BM + nt * 16 + m) * I;
+                    if (c < chunks && pv[nt]) {
+                        rh[j][nt][0] = *(const i32x4*)(hr + k0);
+                        rh[j][nt][1] = *(const i32x4*)(hr + k0 + 8);
+                    } else {
+                        rh[j][nt][0] = i32x4{0, 0, 0, 0};
+                        rh[j][nt][1] = i32x4{0, 0, 0, 0};
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[i] += half2_at(sz + ((size_t)(n0 + 4 * q + i) * groups + g) * 4).x * t4[i];
                 }
             }
-            if (p < NP) {
-                const int t = p / k;
-                const float wt = topk_w[p];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_acc[wv][t][4 * q + i] += wt * acc[i];
+            for (int j = 0; j < G2_MAXC; ++j) {
+                if (c0 + j >= chunks) break;             // uniform over the wave
+                bf16x8 a0, a1;
+                fp8x16_to_bf16(rw[j], a0, a1);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    bf16x8 h0, h1;
+                    split_bf16(rh[j][nt][0], rh[j][nt][1], h0, h1);
+                    acc[nt] = mfma_bf16_16x16x32(a0, h0, acc[nt]);
+                    acc[nt] = mfma_bf16_16x16x32(a1, h1, acc[nt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] *= s2;
+    } else {
+        const uint8_t* wr = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2);
+        const uint8_t* sz = sb + pool.off[1][3];
+        for (int g = 0; g < groups; ++g) {
+            const float z = half2_at(sz + ((size_t)(n0 + m) * groups + g) * 4).y;
+            uint2 rw[2];
+            i32x4 rh[2][NT][2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int k0 = g * 128 + c * 64 + q * 16;
+                rw[c] = *(const uint2*)(wr + k0 / 2);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint16_t* hr = hbuf + (size_t)(b * BM + nt * 16 + m) * I;
+                    if (pv[nt]) {
+                        rh[c][nt][0] = *(const i32x4*)(hr + k0);
+                        rh[c][nt][1] = *(const i32x4*)(hr + k0 + 8);
+                    } else {
+                        rh[c][nt][0] = i32x4{0, 0, 0, 0};
+                        rh[c][nt][1] = i32x4{0, 0, 0, 0};
+                    }
+                }
+            }
+            f32x4 t4[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) t4[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                bf16x8 a0, a1;
+                int4x16_to_bf16(rw[c], z, a0, a1);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    bf16x8 h0, h1;
+                    split_bf16(rh[c][nt][0], rh[c][nt][1], h0, h1);
+                    t4[nt] = mfma_bf16_16x16x32(a0, h0, t4[nt]);
+                    t4[nt] = mfma_bf16_16x16x32(a1, h1, t4[nt]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = half2_at(sz + ((size_t)(n0 + 4 * q + i) * groups + g) * 4).x;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[nt][i] += s * t4[nt][i];
             }
         }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < T * 16; i += G2_THREADS) {
-        const int t = i / 16, c = i % 16;
-        float s = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < G2_WAVES; ++w2) s += s_acc[w2][t][c];
-        out[(size_t)t * H + n0 + c] = f32_to_bf16(s);
+    for (int nt = 0; nt < NT; ++nt)
+        if (pv[nt]) *(f32x4*)(ybuf + (size_t)pr[nt] * H + n0 + 4 * q) = acc[nt] * wt[nt];
+}
+
+// ------------------------------------------------------------ combine
+// out[t] = sum over j of ybuf[t*k + j] in fp32 (fixed order), rounded once to
+// bf16. Pairs with weight exactly 0 (route entries that were never filled)
+// are skipped: their rows were never written.
+template <typename YT, int KMAX>
+__global__ void __launch_bounds__(256) combine_rows_kernel(const YT* __restrict__ ybuf, const float* __restrict__ topk_w,
+                                                          int T, int k, int H, uint16_t* __restrict__ out) {
+    const long n8 = (long)T * (H / 8);
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (long)gridDim.x * blockDim.x) {
+        const int t = (int)(i / (H / 8)), c = (int)(i % (H / 8)) * 8;
+        float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        // every load first (rows of unfilled route entries are read but not used)
+        float wj[KMAX];
+        i32x4 v[KMAX][sizeof(YT) == 4 ? 2 : 1];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            wj[j] = 0.f;
+            if (j < k) {
+                wj[j] = topk_w[(size_t)t * k + j];
+                const YT* row = ybuf + ((size_t)t * k + j) * H + c;
+                v[j][0] = *(const i32x4*)row;
+                if constexpr (sizeof(YT) == 4) v[j][1] = *(const i32x4*)(row + 4);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const bool use = j < k && wj[j] != 0.f;
+            if constexpr (sizeof(YT) == 4) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    s[d] += use ? __int_as_float(v[j][0][d]) : 0.f;
+                    s[4 + d] += use ? __int_as_float(v[j][1][d]) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    s[2 * d] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] & 0xFFFF)) : 0.f;
+                    s[2 * d + 1] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] >> 16)) : 0.f;
+                }
+            }
+        }
+        i32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = (int)two_bf16(s[2 * d], s[2 * d + 1]);
+        *(i32x4*)(out + (size_t)t * H + c) = o;
     }
 }
 
+hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
+                              hipStream_t stream) {
+    const long n8 = (long)T * (H / 8);
+    const int blocks = (int)((n8 + 255) / 256 < 2048 ? (n8 + 255) / 256 : 2048);
+    if (k <= 8)
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 8>), dim3(blocks), dim3(256), 0, stream, ybuf, topk_w,
+                   T, k, H, out);
+    else if (k <= 16)
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 16>), dim3(blocks), dim3(256), 0, stream, ybuf,
+                   topk_w, T, k, H, out);
+    else
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, MOE_MAX_K>), dim3(blocks), dim3(256), 0, stream, ybuf,
+                   topk_w, T, k, H, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
+                               hipStream_t stream) {
+    const long n8 = (long)T * (H / 8);
+    const int blocks = (int)((n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096);
+    if (k <= 8)
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, 8>), dim3(blocks), dim3(256), 0, stream, ybuf,
+                   topk_w, T, k, H, out);
+    else if (k <= 16)
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, 16>), dim3(blocks), dim3(256), 0, stream, ybuf,
+                   topk_w, T, k, H, out);
+    else
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, MOE_MAX_K>), dim3(blocks), dim3(256), 0, stream,
+                   ybuf, topk_w, T, k, H, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ host side
 int stream_max_tokens() { return STREAM_MAX_T; }
 
-size_t stream_workspace_bytes(int cap, int I) { return (size_t)cap * I * sizeof(uint16_t); }
+static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
+    return up256((size_t)cap * I * sizeof(uint16_t)) + up256((size_t)T * k * H * sizeof(float));
+}
+
+template <int BM>
+static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, const float* topk_w,
+                             const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded, int cap,
+                             int H, int I, uint16_t* hbuf, float* ybuf, hipStream_t stream) {
+    const int NP = T * k;
+    const int nb = cap / BM;                        // blocks that can exist; the kernels skip the rest
+    MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(nb * (I / ROWS)), dim3(G_THREADS), 0, stream, sv,
+               n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
+    MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(nb * (H / G2_COLS)), dim3(G_THREADS), 0, stream,
+               sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+}
 
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                              const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
@@ -309,34 +497,18 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
     sv.fmt = pa.fmt;
     for (int f = 0; f < 2; ++f)
         for (int p = 0; p < 4; ++p) sv.off[f][p] = pa.off[f][p];
-    const int H = pa.hidden, I = pa.inter, NP = T * k;
+    const int H = pa.hidden, I = pa.inter;
     uint16_t* hbuf = (uint16_t*)ws;
-    const int units_max = (cap / block_m) * (I / ROWS);
-    dim3 g1(units_max < 4096 ? units_max : 4096);
-    dim3 g2(H / 16);
+    float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
     switch (block_m) {
-        case 16:
-            MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<16>, g1, dim3(G1_THREADS), 0, stream, sv, x, NP, k, sorted_pair,
-                               block_slot, n_padded, H, I, hbuf);
-            MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<16>, g2, dim3(G2_THREADS), 0, stream, sv, T, NP, k, topk_w,
-                               sorted_pair, block_slot, n_padded, H, I, hbuf, out);
-            break;
-        case 32:
-            MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<32>, g1, dim3(G1_THREADS), 0, stream, sv, x, NP, k, sorted_pair,
-                               block_slot, n_padded, H, I, hbuf);
-            MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<32>, g2, dim3(G2_THREADS), 0, stream, sv, T, NP, k, topk_w,
-                               sorted_pair, block_slot, n_padded, H, I, hbuf, out);
-            break;
-        case 64:
-            MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<64>, g1, dim3(G1_THREADS), 0, stream, sv, x, NP, k, sorted_pair,
-                               block_slot, n_padded, H, I, hbuf);
-            MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<64>, g2, dim3(G2_THREADS), 0, stream, sv, T, NP, k, topk_w,
-                               sorted_pair, block_slot, n_padded, H, I, hbuf, out);
-            break;
-        default:
-            return hipErrorInvalidValue;
+        case 16: launch_stream_bm<16>(sv, pa.n_slots, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf, stream); break;
+        case 32: launch_stream_bm<32>(sv, pa.n_slots, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf, stream); break;
+        case 64: launch_stream_bm<64>(sv, pa.n_slots, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf, stream); break;
+        default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_combine_f32(ybuf, topk_w, T, k, H, out, stream);
 }
 
 }  // namespace moe

@@ -12,6 +12,7 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 #define MOE_WAVE 64
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
+#define MOE_MAX_SLOTS 4096     // slots per pool the kernels accept
 #define MOE_ACT_G 128          // activation-scale group along K
 #define MOE_INT4_G 128         // int4 weight group along K
 
@@ -72,6 +73,58 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Wave-wide max of 64-bit keys through DPP row shifts and row broadcasts
+// (lane 63 ends with the maximum, which is then read back to every lane).
+// Lanes whose DPP source lies outside the row contribute the identity 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+    int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    uint32_t slo = (uint32_t)__builtin_amdgcn_update_dpp(0, lo, CTRL, ROW_MASK, 0xF, false);
+    uint32_t shi = (uint32_t)__builtin_amdgcn_update_dpp(0, hi, CTRL, ROW_MASK, 0xF, false);
+    uint64_t o = ((uint64_t)shi << 32) | slo;
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+    v = dpp_max_step<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_max_step<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_max_step<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_max_step<0x118, 0xF>(v);   // row_shr:8  -> lane 15 of each row holds the row max
+    v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3 -> lane 63 holds the max
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Max of 64-bit keys over each row of 16 lanes, left in every lane of the row
+// (butterfly: swap neighbours, swap pairs, rotate by 4, rotate by 8).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_row_max_step(uint64_t v) {
+    uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+    v = dpp_row_max_step<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = dpp_row_max_step<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = dpp_row_max_step<0x124>(v);   // row_ror:4
+    v = dpp_row_max_step<0x128>(v);   // row_ror:8
+    return v;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_sum_step(float v) {
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over each row of 16 lanes, left in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_row_sum_step<0xB1>(v);
+    v = dpp_row_sum_step<0x4E>(v);
+    v = dpp_row_sum_step<0x124>(v);
+    v = dpp_row_sum_step<0x128>(v);
+    return v;
+}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     int l = lane_id();

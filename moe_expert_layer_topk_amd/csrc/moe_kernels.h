@@ -7,7 +7,7 @@
 namespace moe {
 
 // kernel ids for launch tracing (names in profile.hip)
-enum KernelId { K_ROUTE, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
+enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
                 K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_COMBINE, K_DEQUANT, K_COUNT };
 void prof_mark(int kid, hipStream_t s, bool start);
 
@@ -23,6 +23,7 @@ struct PoolArgs {
     const void* base;
     size_t stride;
     const uint8_t* fmt;
+    int n_slots;
     int hidden, inter;
     size_t off[2][4];   // byte offsets of the four arrays, per slot format
 };
@@ -31,13 +32,22 @@ hipError_t launch_route(const float* logits, const uint8_t* mask, int T, int E, 
                         int32_t* err, hipStream_t stream);
 
 int align_single_max_pairs();
+int route_align_fused_max_pairs();
+hipError_t launch_route_align(const float* logits, const uint8_t* mask, int T, int E, int k, int block_m,
+                              const int32_t* slot_of_expert, int32_t* ids, float* w, int32_t* sorted_pair,
+                              int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
+                              int32_t* err, void* ws, hipStream_t stream);
 size_t align_workspace_bytes(int NP, int E);
-hipError_t launch_align(const int32_t* ids, int NP, int E, int block_m, const int32_t* slot_of_expert,
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, const int32_t* slot_of_expert,
                         int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset,
                         int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream);
 
 int stream_max_tokens();
-size_t stream_workspace_bytes(int cap, int I);
+size_t stream_workspace_bytes(int T, int k, int H, int I, int cap);
+hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
+                              hipStream_t stream);
+hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
+                               hipStream_t stream);
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                              const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream);

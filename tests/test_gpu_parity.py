@@ -40,12 +40,12 @@ def check_align(al, ref, block_m):
     assert int(al["err"].item()) == ref["err"]
 
 
-def run_layer(li, bank, dev, block_m, act_mode, sample=None, bank_dev=None, cache=None):
+def run_layer(li, bank, dev, block_m, act_mode, sample=None, bank_dev=None, cache=None, fused=False):
     c = li.cfg
-    _say(f"[layer] {c.name} T={li.T} layer={li.layer} block_m={block_m} act={act_mode}")
+    _say(f"[layer] {c.name} T={li.T} layer={li.layer} block_m={block_m} act={act_mode} fused={fused}")
     pool = device_pool(li, bank, dev, bank_dev)
     x, logits, soe, mask = device_inputs(li, dev)
-    out, (ids, w, rerr), al = moe.layer(pool, x, logits, c.k, soe, block_m, act_mode, mask=mask)
+    out, (ids, w, rerr), al = moe.layer(pool, x, logits, c.k, soe, block_m, act_mode, mask=mask, fused=fused)
     import torch
     torch.cuda.synchronize()
     ref = oracle_layer(li, bank, block_m, act_mode, token_subset=sample, cache=cache)
@@ -131,6 +131,64 @@ def test_align_matches_oracle(gpu, T, k, E, block_m):
     assert torch.equal(al["sorted_pair"][:n], al2["sorted_pair"][:n])   # run-to-run identical
 
 
+@pytest.mark.parametrize("name,T,block_m", [("C0", 16, 16), ("C1", 1, 16), ("C1", 32, 16), ("C3", 32, 32),
+                                            ("C1", 128, 64), ("C2", 2048, 128)])
+def test_route_align_fused(gpu, name, T, block_m):
+    """moe_route_align equals moe_route followed by moe_align (one kernel
+    when T*k <= 1024, the two-kernel path above that)."""
+    c = CONFIGS[name]
+    li = make_layer(c, T, 1)
+    x, logits, soe, mask = device_inputs(li, gpu)
+    ids, w, al = moe.route_align(logits, c.k, block_m, soe, mask=mask)
+    oi, ow, oe = oracle.route(li.logits, li.mask, c.k)
+    assert np.array_equal(ids.cpu().numpy(), oi)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - ow).max() <= W_TOL
+    ref = oracle.align(oi, c.E, block_m, li.slot_of_expert)
+    err = al.pop("err").cpu().numpy()
+    assert err[0] == oe
+    al["err"] = torch_scalar(err[1])
+    check_align(al, ref, block_m)
+
+
+def torch_scalar(v):
+    import torch
+    return torch.tensor([int(v)], dtype=torch.int32)
+
+
+def test_route_align_fused_shortfall(gpu):
+    """Tokens with fewer than k allowed experts: -1 entries are left out of
+    align and counted in both error words."""
+    import torch
+    rng = np.random.default_rng(3)
+    T, E, k = 20, 64, 6
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    mask = np.zeros(E, np.uint8)
+    mask[[1, 5, 9, 30]] = 1
+    soe = rng.permutation(E).astype(np.int32)
+    ids, w, al = moe.route_align(torch.from_numpy(lg).to(gpu), k, 16, torch.from_numpy(soe).to(gpu),
+                                 mask=torch.from_numpy(mask).to(gpu))
+    oi, ow, oe = oracle.route(lg, mask, k)
+    assert np.array_equal(ids.cpu().numpy(), oi)
+    ref = oracle.align(oi, E, 16, soe)
+    err = al.pop("err").cpu().numpy()
+    assert err[0] == oe == T
+    al["err"] = torch_scalar(err[1])
+    check_align(al, ref, 16)
+
+
+def test_align_duplicate_ids_in_a_token(gpu):
+    """An id listed twice by one token (moe_align takes any ids): still the
+    stable counting sort of the oracle."""
+    import torch
+    rng = np.random.default_rng(8)
+    for T in (3, 40, 200):
+        ids = rng.integers(0, 6, size=(T, 4)).astype(np.int32)
+        ids[0] = [2, 2, 5, 2]
+        soe = np.arange(6, dtype=np.int32)
+        al = moe.align(torch.from_numpy(ids).to(gpu), 6, 16, torch.from_numpy(soe).to(gpu))
+        check_align(al, oracle.align(ids, 6, 16, soe), 16)
+
+
 def test_align_invalid_ids(gpu):
     import torch
     ids = np.array([[0, -1], [1, 0], [5, 2]], dtype=np.int32)    # -1 and 5 are outside [0, E)
@@ -183,7 +241,8 @@ def test_layer_c1_decode(gpu, T):
     c = CONFIGS["C1"]
     bank = make_bank(c)
     li = make_layer(c, T, 7)
-    run_layer(li, bank, gpu, 16, 0)
+    run_layer(li, bank, gpu, 16, 0, fused=True)
+    run_layer(li, bank, gpu, 32, 0)
 
 
 def test_layer_c3_masked_decode(gpu):
