@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -62,6 +64,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}))
+        return
     import moe_expert_layer_topk_amd as moe
     from gen import CONFIGS, make_layer, make_bank
     from harness import device_pool, device_inputs, bank_on_device, oracle_layer

@@ -85,6 +85,7 @@ constexpr int G2_COLS = 64;   // hidden rows per gemm2 unit
 constexpr int G2_MAXC = 8;    // 64-wide K chunks per wave issued together
 constexpr int STREAM_MAX_T = 64;
 
+
 // ------------------------------------------------------------ gemm1
 // One unit per workgroup. Round trip 1: n_padded, the block's slot and pair
 // list, and the pool's format tags (into LDS). Round trip 2: every weight
@@ -253,6 +254,198 @@ __global__ void __launch_bounds__(G_THREADS) gemm1_stream_kernel(
     }
 }
 
+// ------------------------------------------------------------ gemm1, pipelined
+// Persistent gate/up kernel for 16-pair blocks (decode batches).
+// * Unit = (block, 8 inter rows): the 16 rows of the matrix-core A tile are
+//   8 gate rows and the 8 matching up rows, so one tile yields both halves of
+//   silu(gate) * up (swapped between lanes l and l ^ 32 in the epilogue).
+// * Each workgroup walks a contiguous range of units, i.e. consecutive 8-row
+//   slices of one expert's w13 at a time; the token rows of a block are
+//   loaded once per block and kept in registers.
+// * While the matrix cores work on unit i, the weight rows and row scales of
+//   unit i+1 are in flight (two register sets alternated by a two-step loop
+//   body). Loads complete in issue order: each step issues the block's token
+//   rows (when the block changes), then unit i+1's weights, then waits for
+//   what it needs, which leaves unit i+1's weights in flight.
+// int4 units are computed without prefetch.
+constexpr int P1_G = 4;          // 128-wide K groups per wave (hidden <= 2048)
+constexpr int P1_ROWS = 8;       // inter rows per unit (gate and up each)
+constexpr int P1_MAXB = 16;      // blocks per workgroup range the LDS tables hold
+
+struct P1W { i32x4 v[P1_G][2]; f32x4 s; };   // [group][chunk] of this lane's row + scales of rows 4q..4q+3
+struct P1X { i32x4 v[P1_G][2][2]; };         // [group][chunk][half] of this lane's token row
+
+// A-tile row of lane m: gate row i0 + m (m < 8) or up row I + i0 + m - 8
+__device__ __forceinline__ int p1_row(int i0, int m, int I) { return m < 8 ? i0 + m : I + i0 + m - 8; }
+
+__device__ __forceinline__ void p1_issue_w(P1W& W, const SlotView& pool, int slot, int i0, int m, int q, int wv,
+                                           int H, int I, int groups) {
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    const float* s13 = (const float*)(sb + pool.off[0][1]);
+    // C rows 4q..4q+3: q = 0, 1 gate rows i0 + 4q..; q = 2, 3 up rows i0 + 4(q-2)..
+    W.s = *(const f32x4*)(s13 + (q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2)));
+    const uint8_t* wr = sb + (size_t)p1_row(i0, m, I) * H;
+#pragma unroll
+    for (int j = 0; j < P1_G; ++j) {
+        const int g = wv + j * G_WAVES;
+        if (g < groups) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) W.v[j][c] = *(const i32x4*)(wr + g * 128 + c * 64 + q * 16);
+        }
+    }
+}
+
+__device__ __forceinline__ void p1_issue_x(P1X& X, const uint16_t* xr, bool valid, int q, int wv, int groups) {
+#pragma unroll
+    for (int j = 0; j < P1_G; ++j) {
+        const int g = wv + j * G_WAVES;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int k0 = g * 128 + c * 64 + q * 16;
+            if (g < groups && valid) {
+                X.v[j][c][0] = *(const i32x4*)(xr + k0);
+                X.v[j][c][1] = *(const i32x4*)(xr + k0 + 8);
+            } else {
+                X.v[j][c][0] = i32x4{0, 0, 0, 0};
+                X.v[j][c][1] = i32x4{0, 0, 0, 0};
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4 p1_mma(const P1W& W, const P1X& X, int wv, int groups) {
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < P1_G; ++j) {
+        if (wv + j * G_WAVES >= groups) break;        // uniform over the wave
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            bf16x8 a0, a1, xb0, xb1;
+            fp8x16_to_bf16(W.v[j][c], a0, a1);
+            split_bf16(X.v[j][c][0], X.v[j][c][1], xb0, xb1);
+            acc = mfma_bf16_16x16x32(a0, xb0, acc);
+            acc = mfma_bf16_16x16x32(a1, xb1, acc);
+        }
+    }
+    return acc;
+}
+
+// int4 unit, synchronous: rows as in p1_row, this wave's groups, scales applied
+__device__ __forceinline__ f32x4 p1_int4(const SlotView& pool, int slot, const P1X& X, int i0, int m, int q, int wv,
+                                         int H, int I, int groups) {
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    const int row = p1_row(i0, m, I);
+    const uint8_t* wr = sb + (size_t)row * (H / 2);
+    const uint8_t* sz = sb + pool.off[1][1];
+    const int orow = q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2);     // first C row this lane holds
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < P1_G; ++j) {
+        const int g = wv + j * G_WAVES;
+        if (g >= groups) break;
+        const float z = half2_at(sz + ((size_t)row * groups + g) * 4).y;
+        f32x4 t4 = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint2 rw = *(const uint2*)(wr + (g * 128 + c * 64 + q * 16) / 2);
+            bf16x8 a0, a1, xb0, xb1;
+            int4x16_to_bf16(rw, z, a0, a1);
+            split_bf16(X.v[j][c][0], X.v[j][c][1], xb0, xb1);
+            t4 = mfma_bf16_16x16x32(a0, xb0, t4);
+            t4 = mfma_bf16_16x16x32(a1, xb1, t4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += half2_at(sz + ((size_t)(orow + i) * groups + g) * 4).x * t4[i];
+    }
+    return acc;
+}
+
+__global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
+    SlotView pool, int n_slots, const uint16_t* __restrict__ x, int NP, int k,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
+    const int32_t* __restrict__ n_padded, int H, int I, uint16_t* __restrict__ hbuf) {
+    __shared__ f32x4 s_red[G_WAVES][MOE_WAVE];
+    __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
+    __shared__ int s_slot[P1_MAXB];
+    __shared__ int s_pr[P1_MAXB][16];
+    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
+    const int m = lane & 15, q = lane >> 4;
+    const int ntile = I / P1_ROWS;
+    const int groups = H / 128;
+    const int n_units = (*n_padded / 16) * ntile;
+    const int per = (n_units + gridDim.x - 1) / gridDim.x;
+    const int u_begin = blockIdx.x * per;
+    const int u_end = min(n_units, u_begin + per);
+    const int b_first = u_begin / ntile;
+    const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
+    // ---- descriptors of my blocks and the format tags: one round trip
+    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+    for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
+        const int bb = i / 17, r = i % 17;
+        if (r == 16) s_slot[bb] = block_slot[b_first + bb];
+        else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
+    }
+    __syncthreads();
+    if (nblk == 0) return;
+    auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
+
+    P1W WA, WB;
+    P1X X;
+    int xblock = -1;
+    {
+        const int s0 = s_slot[0];
+        if (s0 >= 0 && fmt_of(s0) == 0) p1_issue_w(WA, pool, s0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    }
+    auto step = [&](int u, P1W& Wc, P1W& Wn) {
+        const int bb = u / ntile - b_first;
+        const int i0 = (u % ntile) * P1_ROWS;
+        const int slot = s_slot[bb];
+        const int fmt = fmt_of(slot);
+        const int pr = s_pr[bb][m];
+        const bool valid = pr < NP;
+        if (slot >= 0 && bb != xblock) {              // new block: its token rows, before the prefetch
+            p1_issue_x(X, x + (size_t)(valid ? pr / k : 0) * H, valid, q, wv, groups);
+            xblock = bb;
+        }
+        if (u + 1 < u_end) {
+            const int bn = (u + 1) / ntile - b_first;
+            const int sn = s_slot[bn];
+            if (sn >= 0 && fmt_of(sn) == 0)
+                p1_issue_w(Wn, pool, sn, ((u + 1) % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        }
+        if (slot < 0) return;                          // uniform over the workgroup
+        f32x4 acc;
+        if (fmt == 0) {
+            acc = p1_mma(Wc, X, wv, groups) * Wc.s;
+        } else {
+            acc = p1_int4(pool, slot, X, i0, m, q, wv, H, I, groups);
+        }
+        s_red[wv][lane] = acc;
+        __syncthreads();
+        if (wv == 0) {
+            f32x4 v = s_red[0][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < G_WAVES; ++w2) v += s_red[w2][lane];
+            // lanes q = 0, 1 hold gate rows, q = 2, 3 the up rows of the same inter index
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32, 64);
+            if (valid && q < 2) {
+                float hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv[i] = silu(v[i]) * o[i];
+                *(uint2*)(hbuf + (size_t)((b_first + bb) * 16 + m) * I + i0 + 4 * q) =
+                    make_uint2(two_bf16(hv[0], hv[1]), two_bf16(hv[2], hv[3]));
+            }
+        }
+        __syncthreads();
+    };
+    for (int u = u_begin; u < u_end; u += 2) {
+        step(u, WA, WB);
+        if (u + 1 < u_end) step(u + 1, WB, WA);
+    }
+}
+
 // ------------------------------------------------------------ gemm2
 // One unit per workgroup: (block, 64 hidden rows); wave w owns 16 rows.
 // Round trip 1 as in gemm1; round trip 2: W2 row chunks, h rows of the
@@ -387,6 +580,142 @@ __global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
         if (pv[nt]) *(f32x4*)(ybuf + (size_t)pr[nt] * H + n0 + 4 * q) = acc[nt] * wt[nt];
 }
 
+// ------------------------------------------------------------ gemm2, pipelined
+// Persistent down-projection kernel for 16-pair blocks, built like the
+// pipelined gemm1: contiguous unit ranges per workgroup (unit = block x 64
+// hidden rows, wave w owns 16 of them), the block's h rows loaded once per
+// block and kept in registers, the next unit's W2 rows and scales in flight
+// while the current one is multiplied. int4 units run without prefetch.
+constexpr int P2_MAXB = 16;
+
+constexpr int P2_C = 8;          // 64-wide K chunks per wave (inter <= 512)
+
+struct P2W { i32x4 v[P2_C]; f32x4 s; };
+struct P2H { i32x4 v[P2_C][2]; };
+
+__device__ __forceinline__ void p2_issue_w(P2W& W, const SlotView& pool, int slot, int n0, int m, int q, int I,
+                                           int chunks) {
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    W.s = *(const f32x4*)((const float*)(sb + pool.off[0][3]) + n0 + 4 * q);
+    const uint8_t* wr = sb + pool.off[0][2] + (size_t)(n0 + m) * I;
+#pragma unroll
+    for (int c = 0; c < P2_C; ++c)
+        if (c < chunks) W.v[c] = *(const i32x4*)(wr + c * 64 + q * 16);
+}
+
+__device__ __forceinline__ void p2_issue_h(P2H& Hh, const uint16_t* hr, bool valid, int q, int chunks) {
+#pragma unroll
+    for (int c = 0; c < P2_C; ++c) {
+        if (c < chunks && valid) {
+            Hh.v[c][0] = *(const i32x4*)(hr + c * 64 + q * 16);
+            Hh.v[c][1] = *(const i32x4*)(hr + c * 64 + q * 16 + 8);
+        } else {
+            Hh.v[c][0] = i32x4{0, 0, 0, 0};
+            Hh.v[c][1] = i32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+__global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
+    SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
+    const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf) {
+    __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
+    __shared__ int s_slot[P2_MAXB];
+    __shared__ int s_pr[P2_MAXB][16];
+    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
+    const int m = lane & 15, q = lane >> 4;
+    const int ntile = H / G2_COLS;
+    const int chunks = I / 64;
+    const int groups = I / MOE_INT4_G;
+    const int n_units = (*n_padded / 16) * ntile;
+    const int per = (n_units + gridDim.x - 1) / gridDim.x;
+    const int u_begin = blockIdx.x * per;
+    const int u_end = min(n_units, u_begin + per);
+    const int b_first = u_begin / ntile;
+    const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
+    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+    for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
+        const int bb = i / 17, r = i % 17;
+        if (r == 16) s_slot[bb] = block_slot[b_first + bb];
+        else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
+    }
+    __syncthreads();
+    if (nblk == 0) return;
+    auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
+
+    P2W WA, WB;
+    P2H Hh;
+    int hblock = -1;
+    float wt = 0.f;
+    {
+        const int s0 = s_slot[0];
+        if (s0 >= 0 && fmt_of(s0) == 0) p2_issue_w(WA, pool, s0, (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+    }
+    auto step = [&](int u, P2W& Wc, P2W& Wn) {
+        const int bb = u / ntile - b_first;
+        const int n0 = (u % ntile) * G2_COLS + wv * 16;
+        const int slot = s_slot[bb];
+        const int pr = s_pr[bb][m];
+        const bool valid = pr < NP;
+        if (slot >= 0 && bb != hblock) {              // new block: its h rows and route weights
+            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + m) * I, valid, q, chunks);
+            wt = valid ? topk_w[pr] : 0.f;
+            hblock = bb;
+        }
+        if (u + 1 < u_end) {
+            const int sn = s_slot[(u + 1) / ntile - b_first];
+            if (sn >= 0 && fmt_of(sn) == 0)
+                p2_issue_w(Wn, pool, sn, ((u + 1) % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        }
+        float* yrow = ybuf + (size_t)(valid ? pr : 0) * H + n0 + 4 * q;
+        if (slot < 0) {                               // non-resident expert: its pairs add zero
+            if (valid) *(f32x4*)yrow = f32x4{0, 0, 0, 0};
+            return;
+        }
+        f32x4 acc = {0, 0, 0, 0};
+        if (fmt_of(slot) == 0) {
+#pragma unroll
+            for (int c = 0; c < P2_C; ++c) {
+                if (c >= chunks) break;                // uniform
+                bf16x8 a0, a1, h0, h1;
+                fp8x16_to_bf16(Wc.v[c], a0, a1);
+                split_bf16(Hh.v[c][0], Hh.v[c][1], h0, h1);
+                acc = mfma_bf16_16x16x32(a0, h0, acc);
+                acc = mfma_bf16_16x16x32(a1, h1, acc);
+            }
+            acc *= Wc.s;
+        } else {
+            const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+            const uint8_t* wr = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2);
+            const uint8_t* sz = sb + pool.off[1][3];
+#pragma unroll
+            for (int g = 0; g < P2_C / 2; ++g) {
+                if (g >= groups) break;                // uniform
+                const float z = half2_at(sz + ((size_t)(n0 + m) * groups + g) * 4).y;
+                f32x4 t4 = {0, 0, 0, 0};
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const int c = g * 2 + c2;
+                    const uint2 rw = *(const uint2*)(wr + (c * 64 + q * 16) / 2);
+                    bf16x8 a0, a1, h0, h1;
+                    int4x16_to_bf16(rw, z, a0, a1);
+                    split_bf16(Hh.v[c][0], Hh.v[c][1], h0, h1);
+                    t4 = mfma_bf16_16x16x32(a0, h0, t4);
+                    t4 = mfma_bf16_16x16x32(a1, h1, t4);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += half2_at(sz + ((size_t)(n0 + 4 * q + i) * groups + g) * 4).x * t4[i];
+            }
+        }
+        if (valid) *(f32x4*)yrow = acc * wt;
+    };
+    for (int u = u_begin; u < u_end; u += 2) {
+        step(u, WA, WB);
+        if (u + 1 < u_end) step(u + 1, WB, WA);
+    }
+}
+
 // ------------------------------------------------------------ combine
 // out[t] = sum over j of ybuf[t*k + j] in fp32 (fixed order), rounded once to
 // bf16. Pairs with weight exactly 0 (route entries that were never filled)
@@ -470,6 +799,19 @@ hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T,
 // ------------------------------------------------------------ host side
 int stream_max_tokens() { return STREAM_MAX_T; }
 
+// compute units of the current device (cached per device id)
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 
 size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
@@ -482,10 +824,28 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
                              int H, int I, uint16_t* hbuf, float* ybuf, hipStream_t stream) {
     const int NP = T * k;
     const int nb = cap / BM;                        // blocks that can exist; the kernels skip the rest
-    MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(nb * (I / ROWS)), dim3(G_THREADS), 0, stream, sv,
-               n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
-    MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(nb * (H / G2_COLS)), dim3(G_THREADS), 0, stream,
-               sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+    const int units = nb * (I / ROWS);
+    const int pipe_grid = 2 * device_cus();
+    // the pipelined kernel: 16-pair blocks, hidden <= 2048, and each workgroup's
+    // unit range must span at most P1_MAXB blocks (always true unless the grid is tiny)
+    const int pipe_units = nb * (I / P1_ROWS);
+    const int per = (pipe_units + pipe_grid - 1) / pipe_grid;
+    if (BM == 16 && H <= 128 * G_WAVES * P1_G && per / (I / P1_ROWS) + 2 <= P1_MAXB) {
+        MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_pipe_kernel, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
+    } else {
+        MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(units), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
+    }
+    const int units2 = nb * (H / G2_COLS);
+    const int per2 = (units2 + pipe_grid - 1) / pipe_grid;
+    if (BM == 16 && I <= 64 * P2_C && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
+        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv, n_slots,
+                   NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+    } else {
+        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(units2), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+    }
 }
 
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,

@@ -43,6 +43,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, co
                         int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream);
 
 int stream_max_tokens();
+int device_cus();
 size_t stream_workspace_bytes(int T, int k, int H, int I, int cap);
 hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
                               hipStream_t stream);
