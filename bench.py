@@ -206,7 +206,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         rec = json.load(open(tpath)).get(f"{cfg.name}-T{T}-{dom}")
-        if rec and rec.get("source_hash") == source_hash("ffn_stream.hip" if act == moe.ACT_BF16 else "ffn_grouped.hip"):
+        if rec and rec.get("source_hash") == source_hash("ffn_stream.hip" if act == moe.ACT_BF16 else "ffn_mfma.hip"):
             traffic = rec.get("bytes_per_launch")
     roof["traffic"] = traffic
 

@@ -90,7 +90,8 @@ __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t
                                                       const int32_t* __restrict__ sorted_pair,
                                                       const int32_t* __restrict__ block_slot,
                                                       const int32_t* __restrict__ n_padded, int H, int I,
-                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
+                                                      int int4_only) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* sA = smem;                               // [BM][LDS_ROW]
@@ -106,6 +107,7 @@ __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t
     if (slot < 0) return;
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
     const int fmt = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;   // int4 needs inter % 128 == 0
+    if (int4_only && fmt == 0) return;
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int c0 = nt_idx * 128;                      // first inter column of the tile
     const int ncols = min(128, I - c0);               // valid inter columns
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
                                                       const int32_t* __restrict__ block_slot,
                                                       const int32_t* __restrict__ n_padded, int H, int I,
                                                       const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-                                                      uint16_t* __restrict__ ybuf) {
+                                                      uint16_t* __restrict__ ybuf, int int4_only) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* sA = smem;                               // [BM][LDS_ROW]
@@ -285,6 +287,7 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
     const int slot = block_slot[mt_idx];
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int n0 = nt_idx * 128;
+    if (int4_only && (slot < 0 || pool.fmt[slot] != 1 || I % MOE_INT4_G != 0)) return;
     if (slot < 0) {                                   // non-resident expert: its pairs add zero
         for (int i = threadIdx.x; i < BM * 16; i += GT) {
             int r = i >> 4, ch = i & 15;
@@ -421,7 +424,7 @@ static size_t gemm2_smem() {
 }
 
 template <int BM>
-static hipError_t launch_grouped_bm(const GPool& gp, const GroupedWs& w, const uint16_t* x, int T, int k,
+static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const GroupedWs& w, const uint16_t* x, int T, int k,
                                     const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
                                     const int32_t* n_padded, int cap, int H, int I, uint16_t* out,
                                     hipStream_t stream) {
@@ -430,12 +433,27 @@ static hipError_t launch_grouped_bm(const GPool& gp, const GroupedWs& w, const u
     MOE_LAUNCH(K_QUANT_ACT, stream, quant_act_kernel, dim3((unsigned)((qitems + 3) / 4)), dim3(256), 0, stream, x, T, H, w.xq, w.xs);
     dim3 g1((I + 127) / 128, cap / BM);
     size_t sm1 = gemm1_smem<BM>(H);
-    MOE_LAUNCH(K_GEMM1_FP8, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k, sorted_pair,
-                       block_slot, n_padded, H, I, w.hq, w.hs);
     dim3 g2(H / 128, cap / BM);
-    MOE_LAUNCH(K_GEMM2_FP8, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k, topk_w, sorted_pair,
-                       block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (BM == 128 && mfma_path_ok(H, I)) {
+        // FP8 tiles on the pipelined kernels, int4 tiles on the simple ones
+        e = launch_mfma_gemm1(pa, w.xq, w.xs, NP, k, sorted_pair, block_slot, n_padded,
+                              cap, H, I, w.hq, w.hs, stream);
+        if (e != hipSuccess) return e;
+        MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
+                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1);
+        e = launch_mfma_gemm2(pa, NP, topk_w, sorted_pair, block_slot, n_padded, cap,
+                              H, I, w.hq, w.hs, w.ybuf, stream);
+        if (e != hipSuccess) return e;
+        MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
+                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1);
+    } else {
+        MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
+                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 0);
+        MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
+                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 0);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_combine_bf16(w.ybuf, topk_w, T, k, H, out, stream);
 }
@@ -451,10 +469,10 @@ hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int 
         for (int p = 0; p < 4; ++p) gp.off[f][p] = pa.off[f][p];
     GroupedWs w = grouped_ws_layout(ws, T, k, pa.hidden, pa.inter, cap);
     if (block_m == 64)
-        return launch_grouped_bm<64>(gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
+        return launch_grouped_bm<64>(pa, gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
                                      pa.inter, out, stream);
     if (block_m == 128)
-        return launch_grouped_bm<128>(gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
+        return launch_grouped_bm<128>(pa, gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
                                       pa.inter, out, stream);
     return hipErrorInvalidValue;
 }

@@ -210,11 +210,14 @@ def test_layer_c0(gpu, act_mode, block_m):
 
 MID = Config("mid", 70, (300, 50), 256, 128, 16, 4, 1, 0.1, True, slots=0)
 MIX = Config("mix", 71, (200, 40), 256, 128, 16, 4, 1, 0.1, True, slots=0, int4_frac=0.4, resident_all_at=1)
+# several K steps in both products (H / 128 = 4, I / 128 = 3), ragged blocks, int4 mixed in
+WIDE = Config("wide", 72, (700,), 512, 384, 24, 6, 1, 0.1, True, slots=0, int4_frac=0.25, resident_all_at=1)
 
 
 @pytest.mark.parametrize("cfg,T,act_mode,block_m", [(MID, 300, 1, 64), (MID, 300, 1, 128), (MID, 50, 0, 16),
                                                     (MID, 50, 0, 64), (MID, 50, 1, 64), (MIX, 200, 1, 128),
-                                                    (MIX, 40, 0, 16), (MIX, 40, 0, 32), (MIX, 40, 1, 64)])
+                                                    (MIX, 40, 0, 16), (MIX, 40, 0, 32), (MIX, 40, 1, 64),
+                                                    (WIDE, 700, 1, 128), (WIDE, 700, 1, 64)])
 def test_layer_mid_sizes(gpu, cfg, T, act_mode, block_m):
     run_layer(make_layer(cfg, T, 0), make_bank(cfg), gpu, block_m, act_mode)
 
@@ -234,6 +237,15 @@ def test_nonresident_expert_contributes_zero(gpu):
     for act, bm in ((0, 16), (1, 64)):
         out, ref = run_layer(li, make_bank(c), gpu, bm, act)
         assert ref["err"] > 0
+
+
+def test_nonresident_expert_contributes_zero_fp8_tiles(gpu):
+    li = make_layer(WIDE, 700, 1)
+    ids, _, _ = oracle.route(li.logits, None, WIDE.k)
+    for e in (int(ids[0, 0]), int(ids[5, 2])):
+        li.slot_of_expert[e] = -1
+    out, ref = run_layer(li, make_bank(WIDE), gpu, 128, 1)
+    assert ref["err"] > 0
 
 
 @pytest.mark.parametrize("T", [1, 8, 32])
