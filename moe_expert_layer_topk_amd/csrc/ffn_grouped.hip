@@ -287,7 +287,7 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
     const int slot = block_slot[mt_idx];
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int n0 = nt_idx * 128;
-    if (int4_only && (slot < 0 || pool.fmt[slot] != 1 || I % MOE_INT4_G != 0)) return;
+    if (int4_only && slot >= 0 && (pool.fmt[slot] != 1 || I % MOE_INT4_G != 0)) return;   // FP8: elsewhere
     if (slot < 0) {                                   // non-resident expert: its pairs add zero
         for (int i = threadIdx.x; i < BM * 16; i += GT) {
             int r = i >> 4, ch = i & 15;
@@ -392,6 +392,7 @@ static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 struct GroupedWs {
     uint8_t *xq, *xs, *hq, *hs;
     uint16_t* ybuf;
+    void* mm;             // workspace of the pipelined kernels
     size_t total;
 };
 
@@ -404,6 +405,7 @@ static GroupedWs grouped_ws_layout(void* base, int T, int k, int H, int I, int c
     w.hq = p + o; o += up256((size_t)cap * I);
     w.hs = p + o; o += up256((size_t)cap * ((I + MOE_ACT_G - 1) / MOE_ACT_G));
     w.ybuf = (uint16_t*)(p + o); o += up256((size_t)T * k * H * 2);
+    w.mm = p + o; o += up256(mfma_ws_bytes(H, cap));
     w.total = o;
     return w;
 }
@@ -436,14 +438,14 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
     dim3 g2(H / 128, cap / BM);
     hipError_t e;
     if (BM == 128 && mfma_path_ok(H, I)) {
-        // FP8 tiles on the pipelined kernels, int4 tiles on the simple ones
-        e = launch_mfma_gemm1(pa, w.xq, w.xs, NP, k, sorted_pair, block_slot, n_padded,
-                              cap, H, I, w.hq, w.hs, stream);
+        // FP8 blocks on the pipelined kernels; int4 and non-resident blocks on the simple ones
+        e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
+                            w.ybuf, w.mm, 0, stream);
         if (e != hipSuccess) return e;
         MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
                    sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1);
-        e = launch_mfma_gemm2(pa, NP, topk_w, sorted_pair, block_slot, n_padded, cap,
-                              H, I, w.hq, w.hs, w.ybuf, stream);
+        e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
+                            w.ybuf, w.mm, 1, stream);
         if (e != hipSuccess) return e;
         MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
                    topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1);

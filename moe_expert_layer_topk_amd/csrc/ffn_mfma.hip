@@ -6,44 +6,73 @@
 // slot (vllm-expert-pager article, rand.pepabo.com, "hierarchical paging";
 // Table 1 set-up: w13 = gate+up, w2 = down).
 //
-// Both kernels compute a 128 x 256 output tile with 4 waves (2 x 2, 64 x 128
-// per wave, 32 v_mfma_scale_f32_16x16x128_f8f6f4 per 128-wide K step):
-// * operands reach LDS through direct-to-LDS 16-byte loads (no register
-//   staging), 3 stages deep: while step g is multiplied, steps g+1 and g+2
-//   are in flight;
-// * each 128-byte LDS row stores its 16-byte chunks XOR-swizzled by the row
-//   index, chosen through the source address of each lane, so the 16 lanes
-//   reading one fragment column hit different banks;
-// * the tile order is remapped so that the workgroups of one XCD (blocks are
-//   dealt round-robin over the 8 XCDs) work on consecutive tiles: the same
-//   token rows and the same expert's weights stay in that XCD's L2;
-// * the power-of-two activation scales are E8M0 bytes fed to the scaled
-//   matrix instruction, so scaling is free inside the K loop.
-// gemm1 gathers the token rows of a block of pairs and multiplies them by
-// 128 gate and the matching 128 up rows of W13; the epilogue applies the
-// row scales, silu(gate) * up and quantizes h per (row, 128 columns).
-// gemm2 multiplies 128 rows of h by 256 rows of W2 and writes
-// w[t][j] * y, in bf16, to the pair's row of the combine buffer.
-// Tiles whose slot is stored int4-g128 are skipped here; the simpler kernels
-// of ffn_grouped.hip, launched in their int4-only mode, multiply those.
+// gemm1 multiplies the gathered token rows of a 128-row block by 128 gate and
+// the matching 128 up rows of W13; its epilogue applies the row scales,
+// silu(gate) * up and quantizes h per (row, 128 columns). gemm2 multiplies
+// 128 rows of h by 256 rows of W2 and writes w[t][j] * y, in bf16, to the
+// pair's row of the combine buffer. Both are built the same way:
+// * persistent: one workgroup per CU walks a list of (block, column tile)
+//   tiles; the workgroups of one XCD (blocks are dealt round-robin over the 8
+//   XCDs) take consecutive tiles, so the same token rows and the same
+//   expert's weights are shared in that XCD's L2;
+// * the K steps of all tiles of a workgroup form one stream: a ring of three
+//   LDS stages is filled by direct-to-LDS 16-byte loads; while step s is
+//   multiplied from registers, the fragments of step s+1 are read from LDS
+//   and steps s+2 and s+3 are in flight, also across tile boundaries, so the
+//   next tile's loads hide behind the current tile's last steps and epilogue;
+// * a stage holds 128 A rows and 256 B rows of 128 bytes; one 16-byte load
+//   instruction fills 8 whole rows (full 128-byte lines from memory), each
+//   row's 16-byte chunks XOR-swizzled by the row index through the source
+//   address of each lane, so that the 16 lanes reading one fragment column
+//   spread over the LDS banks;
+// * 4 waves in a 2 x 2 grid, 64 x 128 outputs each: 32
+//   v_mfma_scale_f32_16x16x128_f8f6f4 per K step, with the power-of-two
+//   activation exponents (E8M0) as the instruction's A scales;
+// * B rows are ordered so that the four accumulators a lane holds for one
+//   row across four fragments are adjacent output columns: epilogue stores
+//   are 4-byte fp8 or 8-byte bf16 runs straight from registers;
+// * per-tile metadata (row scales of the expert, pair ids, route weights)
+//   reaches LDS by direct-to-LDS loads issued with the tile's first stage,
+//   and token ids are read with scalar loads, so no vector load ever waits
+//   behind the stages in flight.
+// A prep kernel lists the FP8 blocks and lays out the per-position token
+// ids, route weights and activation scales the two kernels read. Blocks whose
+// slot is int4-g128 or not resident are handled by the simpler kernels of
+// ffn_grouped.hip in their int4-only mode.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
 constexpr int MM_BM = 128;
-constexpr int MM_BN = 256;
-constexpr int MM_BK = 128;
-constexpr int MM_ST = 3;
 constexpr int MM_THREADS = 256;
-constexpr int MM_STAGE = (MM_BM + MM_BN) * MM_BK;   // 48 KiB: A rows, then B rows
-constexpr int MM_DMA = (MM_BM + MM_BN) / 4 / 8;       // direct-to-LDS loads per wave per stage
+constexpr int MM_RING = 3;                              // LDS stages
+constexpr int MM_OPS = (128 + 256) * 128;               // 128 A rows, 256 B rows of 128 bytes
+constexpr int MM_SCL = MM_OPS;                          // 128 row-scale bytes (+128 unused)
+constexpr int MM_STAGE = MM_OPS + 256;
+constexpr int MM_META = 2048;                           // per-tile metadata slot
+constexpr int MM_NMETA = 4;                             // tiles that can be in flight at once
+constexpr int MM_AMAX = MM_RING * MM_STAGE + MM_NMETA * MM_META;
+constexpr int MM_SMEM = MM_AMAX + 2 * MM_BM * 4;
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
 
 struct MPool {
     const uint8_t* base;
     size_t stride;
-    const uint8_t* fmt;
-    size_t off[2][4];
+    size_t off[4];            // FP8 slot: w13, s13, w2, s2
+};
+
+struct MTiles {
+    const int2* tiles;        // (block, slot) of each FP8 block, in order
+    const int* n_tiles;
+    const int32_t* tokrow;    // token of each sorted position (0 for padding)
+    const float* wsort;       // route weight of each sorted position (0 for padding)
+    const int32_t* sorted_pair;
+    const uint8_t* scl;       // A scale bytes, [block][K step][128 rows]
 };
 
 // s_waitcnt with only vmcnt limited (expcnt and lgkmcnt left open)
@@ -52,341 +81,410 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Leave at most n of this wave's vector memory operations outstanding
+// (waits for all of them when n is outside the table: never too few).
+#define MM_W(n) \
+    case n: wait_vm<n>(); break;
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+        MM_W(0) MM_W(12) MM_W(13) MM_W(14) MM_W(15) MM_W(16) MM_W(24) MM_W(25) MM_W(26) MM_W(27) MM_W(28)
+        MM_W(29) MM_W(30) MM_W(31) MM_W(32)
+        default: wait_vm<0>(); break;
+    }
+}
+#undef MM_W
 
 // Workgroup barrier without the release fence that __syncthreads() adds: that
 // fence waits for every outstanding global load, direct-to-LDS ones included,
-// which would drain the stages still in flight. Callers order their own LDS
-// traffic with wait_vm / lgkmcnt before it.
+// which would drain the stages in flight. The wave's own LDS traffic is
+// waited for first; direct-to-LDS data is waited for with wait_vm before it.
 __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until the oldest stage in flight has landed, leaving the `ahead` stages
-// issued after it outstanding (loads of one wave complete in issue order).
-__device__ __forceinline__ void wait_stage(int ahead) {
-    if (ahead >= 2) wait_vm<2 * MM_DMA>();
-    else if (ahead == 1) wait_vm<MM_DMA>();
-    else wait_vm<0>();
+// lane i writes 16 (4) bytes at lds + 16 i (4 i); lds is wave-uniform
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// Scalar loads for per-tile metadata. A vector load here would be waited for
+// with the direct-to-LDS loads in flight (vector memory completes in order),
+// draining the pipeline; scalar loads count on a separate counter.
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ int2 sload2(const int2* p) {
+    long long r;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return make_int2((int)r, (int)(r >> 32));
+}
+__device__ __forceinline__ i32x16 sload16(const int32_t* p) {
+    i32x16 r;
+    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return r;
 }
 
-// tile id such that the workgroups of one XCD take consecutive tiles
-__device__ __forceinline__ int xcd_tile(int bid, int G) {
-    const int x = bid & 7, idx = bid >> 3, per = G >> 3, rem = G & 7;
-    return x * per + (x < rem ? x : rem) + idx;
-}
-
-// 32 codes of LDS row r (128-byte rows, swizzled chunks), K bytes [32q, 32q+32)
-__device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int r, int q) {
-    const int sw = r & 7;
-    const i32x4 lo = *(const i32x4*)(st + r * 128 + (((2 * q) ^ sw) << 4));
-    const i32x4 hi = *(const i32x4*)(st + r * 128 + (((2 * q + 1) ^ sw) << 4));
+// 32 codes of stage row r for the lane group q (K bytes [32 q, 32 q + 32)):
+// o0, o1 are the lane's swizzled offsets of chunks 2q and 2q+1 (rows read by
+// a lane all share r % 8 = m % 8)
+__device__ __forceinline__ i32x8 frag_read(const uint8_t* st, int r, int o0, int o1) {
+    const i32x4 lo = *(const i32x4*)(st + r * 128 + o0);
+    const i32x4 hi = *(const i32x4*)(st + r * 128 + o1);
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// One wave's share of a stage: rows [row0, row0 + 8N) of an operand, 8 rows
-// per instruction; lane i fills LDS chunk i % 8 of row row0 + 8j + i / 8 with
-// the global chunk that the swizzle puts there.
-template <int N>
-__device__ __forceinline__ void dma_rows(uint8_t* st, int row0, int lane, const uint8_t* const (&src_row)[N],
-                                         int k0) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-        const int r = row0 + j * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        lds_dma16(src_row[j] + k0 + c * 16, st + (row0 + j * 8) * 128);
-    }
+// max over each row of 16 lanes (quad swaps, then row rotations by 4 and 8)
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true)));
+    return v;
 }
 
-// ---------------------------------------------------------------- gemm1
+// two fp32 -> packed bf16, round to nearest even (hardware conversion)
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
 
-__global__ void __launch_bounds__(MM_THREADS, 1) gemm1_mfma_kernel(MPool pool, const uint8_t* __restrict__ xq,
-                                                                  const uint8_t* __restrict__ xs, int NP, int k,
-                                                                  const int32_t* __restrict__ sorted_pair,
-                                                                  const int32_t* __restrict__ block_slot,
-                                                                  const int32_t* __restrict__ n_padded, int H,
-                                                                  int I, uint8_t* __restrict__ hq,
-                                                                  uint8_t* __restrict__ hs) {
+// silu with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------ prep
+// Block 0 lists, in order, the blocks whose slot is resident and FP8; the
+// other blocks write, per sorted position, the token, the route weight and
+// the token's activation scale bytes transposed to [block][K step][row].
+__global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restrict__ sorted_pair,
+                                                       const int32_t* __restrict__ block_slot,
+                                                       const uint8_t* __restrict__ fmt,
+                                                       const int32_t* __restrict__ n_padded, int NP, int k,
+                                                       const float* __restrict__ topk_w,
+                                                       const uint8_t* __restrict__ xs, int groups,
+                                                       int2* __restrict__ tiles, int* __restrict__ n_tiles,
+                                                       int32_t* __restrict__ tokrow, float* __restrict__ wsort,
+                                                       uint8_t* __restrict__ scl) {
+    const int np = *n_padded;
+    if (blockIdx.x == 0) {
+        __shared__ int s_cnt[4];
+        const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
+        const int nb = np / MM_BM;
+        int base = 0;
+        for (int b0 = 0; b0 < nb; b0 += 256) {
+            const int b = b0 + threadIdx.x;
+            const int slot = b < nb ? block_slot[b] : -1;
+            const bool f = slot >= 0 && fmt[slot] == 0;
+            const uint64_t bal = __ballot(f);
+            if (lane == 0) s_cnt[wv] = __popcll(bal);
+            __syncthreads();
+            int off = base;
+            for (int w = 0; w < wv; ++w) off += s_cnt[w];
+            if (f) tiles[off + __popcll(bal & lanemask_lt())] = make_int2(b, slot);
+            base += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) *n_tiles = base;
+        return;
+    }
+    const int pos = (blockIdx.x - 1) * 256 + threadIdx.x;
+    if (pos >= np) return;
+    const int p = sorted_pair[pos];
+    const bool v = p < NP;
+    const int t = v ? p / k : 0;
+    tokrow[pos] = t;
+    wsort[pos] = v ? topk_w[p] : 0.f;
+    const int mt = pos / MM_BM, r = pos % MM_BM;
+    for (int g = 0; g < groups; ++g)
+        scl[((size_t)mt * groups + g) * MM_BM + r] = v ? xs[(size_t)t * groups + g] : (uint8_t)127;
+}
+
+// ------------------------------------------------------------------ gemm kernels
+// KIND 0: gate/up (gemm1), KIND 1: down (gemm2).
+template <int KIND>
+__global__ void __launch_bounds__(MM_THREADS, 1)
+    mfma_ffn_kernel(MPool pool, MTiles tl, const uint8_t* __restrict__ xq, int NP, int H, int I,
+                    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ ybuf) {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int NT = (I + 127) / 128;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = tile / NT, nt = tile % NT;
-    if (mt >= *n_padded / MM_BM) return;
-    const int slot = block_slot[mt];
-    if (slot < 0) return;
-    const int groups = H / 128;
-    uint8_t* st0 = smem;
-    int* s_tok = (int*)(smem + MM_ST * MM_STAGE);               // [128]
-    float* s_amax = (float*)(s_tok + MM_BM);                    // [2][128]
-    uint8_t* s_xs = (uint8_t*)(s_amax + 2 * MM_BM);             // [128][groups]
-    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
+    const int m = lane & 15, q = lane >> 4;
     const int mw = wv & 1, nw = wv >> 1;
-    const int c0 = nt * 128;
-    const int ncols = min(128, I - c0);
-    if (threadIdx.x < MM_BM) {
-        const int p = sorted_pair[mt * MM_BM + threadIdx.x];
-        s_tok[threadIdx.x] = p < NP ? p / k : -1;
-    }
-    if (pool.fmt[slot] == 1) return;                  // int4 slot
-    __syncthreads();
-    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    for (int i = threadIdx.x; i < MM_BM * groups; i += MM_THREADS) {
-        const int r = i / groups, g = i % groups;
-        const int t = s_tok[r];
-        s_xs[i] = t >= 0 ? xs[(size_t)t * groups + g] : (uint8_t)127;
-    }
-    // source rows of this wave's DMA share: A rows [32 wv, 32 wv + 32), B rows [64 wv, 64 wv + 64)
-    const uint8_t* srcA[4];
-    const uint8_t* srcB[8];
+    const int S = KIND == 0 ? H / 128 : I / 128;          // K steps per tile
+    const int NT = KIND == 0 ? I / 128 : H / 256;         // column tiles per block
+    const int hgroups = I / 128;
+
+    // this workgroup's tiles: start + idx + per_x * j, j < nj
+    const int G = *tl.n_tiles * NT;
+    const int x = blockIdx.x & 7, idx = blockIdx.x >> 3, per_x = gridDim.x >> 3;
+    const int gper = G >> 3, grem = G & 7;
+    const int start = x * gper + (x < grem ? x : grem);
+    const int cnt = gper + (x < grem ? 1 : 0);
+    const int nj = cnt > idx ? (cnt - idx + per_x - 1) / per_x : 0;
+    if (nj == 0) return;
+    const int N = nj * S;
+
+    // metadata loads of this wave per tile (256-byte dword loads) and their LDS offset
+    const int meta_n = KIND == 0 ? (wv == 1 || wv == 2 ? 2 : 0) : (wv == 1 || wv == 2 ? 2 : (wv == 3 ? 4 : 0));
+    const int meta_off = KIND == 0 ? (wv == 2 ? 512 : 0) : (wv == 2 ? 512 : (wv == 3 ? 1024 : 0));
+
+    // ---- issue side: sources of the tile being loaded. Wave w loads A rows
+    // 32 w + 8 j + i / 8 (j < 4) and B rows 64 w + 8 j + i / 8 (j < 8); lane i
+    // puts the source chunk cs = (i % 8) ^ (i / 8) of its row at chunk i % 8.
+    const int csw = 16 * ((lane & 7) ^ (lane >> 3));
+    const uint8_t* pA[4];
+    const uint8_t* pB0 = nullptr;         // B row of j = 0; row of j is + (32 (j & 1) + (j >> 1)) rows
+    const uint8_t* pS = nullptr;          // row-scale bytes (wave 0)
+    const uint8_t* pM = nullptr;          // metadata (meta_n > 0)
+    // B stage row 64 w + 8 j + i / 8 = fragment 4 w + j / 2, fragment row 8 (j & 1) + i / 8;
+    // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
+    // (KIND 0: n / 4 picks gate or up rows, CW = 64; KIND 1: CW = 128)
+    const int brow0 = (KIND == 0 ? (wv & 1) * I + (wv >> 1) * 64 : (wv >> 1) * 128 + (wv & 1) * 64) + 4 * (lane >> 3);
+    auto setup = [&](int j) __attribute__((always_inline)) {
+        const int L = start + idx + per_x * j;
+        const int2 d = sload2(tl.tiles + L / NT);
+        const int mt = d.x, nt = L % NT;
+        const uint8_t* sb = pool.base + (size_t)d.y * pool.stride;
+        pS = tl.scl + (size_t)mt * S * MM_BM + 4 * (lane & 31);
+        if (KIND == 0) {
+            // tokens of rows 32 wv .. 32 wv + 31, scalar loads
+            const i32x16 ta = sload16(tl.tokrow + mt * MM_BM + 32 * wv);
+            const i32x16 tb = sload16(tl.tokrow + mt * MM_BM + 32 * wv + 16);
+            const int r8 = lane >> 3;
+            int t[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int t = s_tok[wv * 32 + j * 8 + (lane >> 3)];
-        srcA[j] = xq + (size_t)(t < 0 ? 0 : t) * H;            // padding rows read token 0; outputs unused
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int rb = wv * 64 + j * 8 + (lane >> 3);
-        const int col = rb & 127;
-        const int wrow = (rb < 128 ? 0 : I) + c0 + (col < ncols ? col : 0);
-        srcB[j] = sb + (size_t)wrow * H;
-    }
-    auto issue = [&](int g) {
-        uint8_t* st = st0 + (g % MM_ST) * MM_STAGE;
-        dma_rows<4>(st, wv * 32, lane, srcA, g * 128);
-        dma_rows<8>(st + MM_BM * 128, wv * 64, lane, srcB, g * 128);
-    };
-    f32x4 acc[4][8];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
-    for (int g = 0; g < MM_ST - 1 && g < groups; ++g) issue(g);
-    for (int g = 0; g < groups; ++g) {
-        wait_stage(min(MM_ST - 2, groups - 1 - g));
-        barrier_lds();
-        if (g + MM_ST - 1 < groups) issue(g + MM_ST - 1);
-        const uint8_t* st = st0 + (g % MM_ST) * MM_STAGE;
-        const uint8_t* sB = st + MM_BM * 128;
-        i32x8 bf[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            // n < 4: gate rows nw*64 + 16n; n >= 4: up rows 128 + nw*64 + 16(n-4)
-            const int rb = (n < 4 ? 0 : 128) + nw * 64 + (n & 3) * 16 + m;
-            bf[n] = lds_frag(sB, rb, q);
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int r = mw * 64 + a * 16 + m;
-            const i32x8 af = lds_frag(st, r, q);
-            const int sa = s_xs[r * groups + g];
-#pragma unroll
-            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(af, bf[n], acc[a][n], sa, 127);
-        }
-    }
-    // ---- epilogue: row scales, silu(gate) * up, per-(row, 128 columns) power-of-two quantization
-    const float* s13 = (const float*)(sb + pool.off[0][1]);
-    float sg[4], su[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int col = nw * 64 + n * 16 + m;
-        const bool ok = col < ncols;
-        sg[n] = ok ? s13[c0 + col] : 0.f;
-        su[n] = ok ? s13[I + c0 + col] : 0.f;
-    }
-    float hv[4][4][4];
-    float rmax[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx = 0.f;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const float h = silu(acc[a][n][i] * sg[n]) * (acc[a][n + 4][i] * su[n]);
-                hv[a][n][i] = h;
-                mx = fmaxf(mx, fabsf(h));
+            for (int r = 0; r < 8; ++r) {
+                t[0] = r8 == r ? ta[r] : t[0];
+                t[1] = r8 == r ? ta[8 + r] : t[1];
+                t[2] = r8 == r ? tb[r] : t[2];
+                t[3] = r8 == r ? tb[8 + r] : t[3];
             }
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-            rmax[a][i] = mx;
+            for (int j2 = 0; j2 < 4; ++j2) pA[j2] = xq + (size_t)t[j2] * H + csw;
+            const int c0 = nt * 128;
+            pB0 = sb + pool.off[0] + (size_t)(brow0 + c0) * H + csw;
+            const float* s13 = (const float*)(sb + pool.off[1]);
+            pM = (const uint8_t*)(s13 + (wv == 2 ? I : 0) + c0 + lane);
+        } else {
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2)
+                pA[j2] = hq + (size_t)(mt * MM_BM + 32 * wv + 8 * j2 + (lane >> 3)) * I + csw;
+            const int n0 = nt * 256;
+            pB0 = sb + pool.off[2] + (size_t)(brow0 + n0) * I + csw;
+            if (wv == 1) pM = (const uint8_t*)(tl.sorted_pair + mt * MM_BM + lane);
+            else if (wv == 2) pM = (const uint8_t*)(tl.wsort + mt * MM_BM + lane);
+            else pM = (const uint8_t*)((const float*)(sb + pool.off[3]) + n0 + lane);
         }
-    if (m == 0) {
+    };
+    // vector memory operations stage s puts in flight for this wave
+    auto stage_ops = [&](int s) __attribute__((always_inline)) { return 12 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n : 0); };
+    // The k-th load of stage s for this wave: A rows (k < 4), B rows (k < 12),
+    // then the row scales (wave 0) and, on a tile's first stage, metadata.
+    auto issue_one = [&](int s, int k) __attribute__((always_inline)) {
+        const int g = s % S;
+        uint8_t* st = smem + (s % MM_RING) * MM_STAGE;
+        const int k0 = g * 128;
+        const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
+        if (k < 4) {
+            dma16(pA[k] + k0, st + (32 * wv + 8 * k) * 128);
+        } else if (k < 12) {
+            const int j2 = k - 4;
+            dma16(pB0 + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0, st + MM_BM * 128 + (64 * wv + 8 * j2) * 128);
+        } else if (wv == 0) {
+            if (k == 12) dma4(pS + g * MM_BM, st + MM_SCL);
+        } else if (g == 0 && k - 12 < meta_n) {
+            uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
+            dma4(pM + 256 * (k - 12), md + 256 * (k - 12));
+        }
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        if (s % S == 0) setup(s / S);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) issue_one(s, k);
+    };
+
+    // ---- compute side
+    f32x4 acc[4][8];
+    i32x8 FA[4], FB[8];
+    int SA[4];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_amax[nw * MM_BM + mw * 64 + a * 16 + 4 * q + i] = rmax[a][i];
-    }
-    __syncthreads();                                   // also: every wave is done with the stages
-    uint8_t* sH = st0;                                 // [128 rows][128 B] codes
-    const int hgroups = (I + MOE_ACT_G - 1) / MOE_ACT_G;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = mw * 64 + a * 16 + 4 * q + i;
-            int e = pow2_exponent_448(fmaxf(s_amax[row], s_amax[MM_BM + row]));
-            e = e < -127 ? -127 : (e > 127 ? 127 : e);
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-                sH[row * 128 + nw * 64 + n * 16 + m] = (uint8_t)(f32x2_to_e4m3(ldexpf(hv[a][n][i], -e), 0.f) & 0xFF);
-            if (nw == 0 && m == 0) hs[(size_t)(mt * MM_BM + row) * hgroups + nt] = (uint8_t)(e + 127);
-        }
-    __syncthreads();
-    for (int i = threadIdx.x; i < MM_BM * 8; i += MM_THREADS) {
-        const int r = i >> 3, ch = i & 7;
-        if (ch * 16 < ncols)
-            *(i32x4*)(hq + (size_t)(mt * MM_BM + r) * I + c0 + ch * 16) = *(const i32x4*)(sH + r * 128 + ch * 16);
-    }
-}
-
-// ---------------------------------------------------------------- gemm2
-
-__global__ void __launch_bounds__(MM_THREADS, 1) gemm2_mfma_kernel(MPool pool, int NP, const float* __restrict__ topk_w,
-                                                                  const int32_t* __restrict__ sorted_pair,
-                                                                  const int32_t* __restrict__ block_slot,
-                                                                  const int32_t* __restrict__ n_padded, int H,
-                                                                  int I, const uint8_t* __restrict__ hq,
-                                                                  const uint8_t* __restrict__ hs,
-                                                                  uint16_t* __restrict__ ybuf) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int NT = H / MM_BN;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = tile / NT, nt = tile % NT;
-    if (mt >= *n_padded / MM_BM) return;
-    const int slot = block_slot[mt];
-    const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
-    const int mw = wv & 1, nw = wv >> 1;
-    const int n0 = nt * MM_BN;
-    int* s_pr = (int*)(smem + MM_ST * MM_STAGE);              // [128]
-    float* s_w = (float*)(s_pr + MM_BM);                       // [128]
-    uint8_t* s_hs = (uint8_t*)(s_w + MM_BM);                   // [128][I / 128]
-    if (threadIdx.x < MM_BM) {
-        const int p = sorted_pair[mt * MM_BM + threadIdx.x];
-        s_pr[threadIdx.x] = p;
-        s_w[threadIdx.x] = p < NP ? topk_w[p] : 0.f;
-    }
-    __syncthreads();
-    if (slot < 0) {                                   // non-resident expert: its pairs add zero
-        for (int i = threadIdx.x; i < MM_BM * (MM_BN / 8); i += MM_THREADS) {
-            const int r = i / (MM_BN / 8), ch = i % (MM_BN / 8);
-            const int p = s_pr[r];
-            if (p < NP) *(i32x4*)(ybuf + (size_t)p * H + n0 + ch * 8) = i32x4{0, 0, 0, 0};
-        }
-        return;
-    }
-    if (pool.fmt[slot] == 1) return;                  // int4 slot
-    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int steps = I / 128;
-    const int hgroups = I / MOE_ACT_G;
-    for (int i = threadIdx.x; i < MM_BM * hgroups; i += MM_THREADS) s_hs[i] = hs[(size_t)mt * MM_BM * hgroups + i];
-    const uint8_t* srcA[4];
-    const uint8_t* srcB[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) srcA[j] = hq + (size_t)(mt * MM_BM + wv * 32 + j * 8 + (lane >> 3)) * I;
-    const uint8_t* w2 = sb + pool.off[0][2];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) srcB[j] = w2 + (size_t)(n0 + wv * 64 + j * 8 + (lane >> 3)) * I;
-    auto issue = [&](int g) {
-        uint8_t* st = smem + (g % MM_ST) * MM_STAGE;
-        dma_rows<4>(st, wv * 32, lane, srcA, g * 128);
-        dma_rows<8>(st + MM_BM * 128, wv * 64, lane, srcB, g * 128);
+            for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
-    f32x4 acc[4][8];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
-    for (int g = 0; g < MM_ST - 1 && g < steps; ++g) issue(g);
-    for (int g = 0; g < steps; ++g) {
-        wait_stage(min(MM_ST - 2, steps - 1 - g));
-        barrier_lds();
-        if (g + MM_ST - 1 < steps) issue(g + MM_ST - 1);
-        const uint8_t* st = smem + (g % MM_ST) * MM_STAGE;
-        const uint8_t* sB = st + MM_BM * 128;
-        i32x8 bf[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) bf[n] = lds_frag(sB, nw * 128 + n * 16 + m, q);
+    const int o0 = ((2 * q) ^ (m & 7)) << 4, o1 = ((2 * q + 1) ^ (m & 7)) << 4;
+    auto read_a = [&](const uint8_t* st, int a) __attribute__((always_inline)) {
+        FA[a] = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
+        SA[a] = st[MM_SCL + 64 * mw + 16 * a + m];
+    };
+    auto read_b = [&](const uint8_t* st, int n) __attribute__((always_inline)) {
+        FB[n] = frag_read(st + MM_BM * 128, 16 * (8 * nw + n) + m, o0, o1);
+    };
+    // Multiply the fragments in registers; when `next` is set, refill each
+    // fragment register from stage `next` once its last use has been issued.
+    // Multiply the fragments in registers; with `refill`, reload each
+    // fragment register from stage `next` once its last use has been issued.
+    auto multiply = [&](auto refill, const uint8_t* next) __attribute__((always_inline)) {
+        constexpr bool R = decltype(refill)::value != 0;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const int r = mw * 64 + a * 16 + m;
-            const i32x8 af = lds_frag(st, r, q);
-            const int sa = s_hs[r * hgroups + g];
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(af, bf[n], acc[a][n], sa, 127);
+            for (int n = 0; n < 8; ++n) {
+                acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+                if (R && a == 3) read_b(next, n);
+            }
+            if (R) read_a(next, a);
+        }
+    };
+    auto epilogue = [&](int j) __attribute__((always_inline)) {
+        const int L = start + idx + per_x * j;
+        const int mt = sload2(tl.tiles + L / NT).x, nt = L % NT;
+        const uint8_t* md = smem + MM_RING * MM_STAGE + (j % MM_NMETA) * MM_META;
+        if (KIND == 0) {
+            float* s_amax = (float*)(smem + MM_AMAX);
+            const f32x4 sg = *(const f32x4*)(md + 4 * (nw * 64 + 4 * m));
+            const f32x4 su = *(const f32x4*)(md + 512 + 4 * (nw * 64 + 4 * m));
+            // h replaces the gate accumulators
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float mx = 0.f;
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const float h = silu_rcp(acc[a][n][i] * sg[n]) * (acc[a][n + 4][i] * su[n]);
+                        acc[a][n][i] = h;
+                        mx = fmaxf(mx, fabsf(h));
+                    }
+                    mx = row16_max(mx);
+                    if (m == 0) s_amax[nw * MM_BM + 64 * mw + 16 * a + 4 * q + i] = mx;
+                }
+            barrier_lds();
+            const int c = nt * 128 + nw * 64 + 4 * m;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 64 * mw + 16 * a + 4 * q + i;
+                    int e = pow2_exponent_448(fmaxf(s_amax[row], s_amax[MM_BM + row]));
+                    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+                    const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
+                    const uint32_t hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
+                    *(uint32_t*)(hq + (size_t)(mt * MM_BM + row) * I + c) = lo | (hi << 16);
+                    if (nw == 0 && m == 0) hs[((size_t)mt * hgroups + nt) * MM_BM + row] = (uint8_t)(e + 127);
+                }
+        } else {
+            const int32_t* s_pr = (const int32_t*)md;
+            const float* s_w = (const float*)(md + 512);
+            const f32x4 sc0 = *(const f32x4*)(md + 1024 + 4 * (nw * 128 + 4 * m));
+            const f32x4 sc1 = *(const f32x4*)(md + 1024 + 4 * (nw * 128 + 64 + 4 * m));
+            const int c = nt * 256 + nw * 128 + 4 * m;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 64 * mw + 16 * a + 4 * q + i;
+                    const int p = s_pr[row];
+                    const float w = s_w[row];
+                    uint32_t v[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4 sc = h ? sc1 : sc0;
+                        const float y0 = acc[a][4 * h][i] * sc[0] * w, y1 = acc[a][4 * h + 1][i] * sc[1] * w;
+                        const float y2 = acc[a][4 * h + 2][i] * sc[2] * w, y3 = acc[a][4 * h + 3][i] * sc[3] * w;
+                        v[2 * h] = bf16x2_rne(y0, y1);
+                        v[2 * h + 1] = bf16x2_rne(y2, y3);
+                    }
+                    if (p < NP) {
+                        uint16_t* yr = ybuf + (size_t)p * H + c;
+                        *(uint2*)yr = make_uint2(v[0], v[1]);
+                        *(uint2*)(yr + 64) = make_uint2(v[2], v[3]);
+                    }
+                }
+        }
+    };
+
+    // ---- the stream of K steps
+    zero_acc();
+    int is = 0;
+    for (; is < MM_RING && is < N; ++is) issue(is);
+    {
+        int after = 0;                                  // issued after stage 0
+        for (int s = 1; s < is; ++s) after += stage_ops(s);
+        wait_vm_n(after);
+        barrier_lds();
+        const uint8_t* st = smem;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) read_b(st, n);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) read_a(st, a);
+    }
+    for (int cs = 0; cs + 1 < N; ++cs) {
+        wait_vm_n(cs + 2 < is ? stage_ops(cs + 2) : 0);   // stage cs+1 landed
+        barrier_lds();                                  // ... for every wave; stage cs's buffer is free
+        if (is < N) {
+            issue(is);
+            ++is;
+        }
+        multiply(IC<1>{}, smem + ((cs + 1) % MM_RING) * MM_STAGE);
+        if (cs % S == S - 1) {
+            epilogue(cs / S);
+            zero_acc();
         }
     }
-    // ---- epilogue: row scale x route weight, bf16 rows staged in LDS for 512-byte row stores
-    const float* s2 = (const float*)(sb + pool.off[0][3]);
-    float sc[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) sc[n] = s2[n0 + nw * 128 + n * 16 + m];
-    __syncthreads();                                   // every wave is done with the stages
-    uint16_t* sY = (uint16_t*)smem;                    // [128][256 + 8] bf16
-    constexpr int YROW = MM_BN + 8;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = mw * 64 + a * 16 + 4 * q + i;
-            const float wt = s_w[row];
-#pragma unroll
-            for (int n = 0; n < 8; ++n) sY[row * YROW + nw * 128 + n * 16 + m] = f32_to_bf16(acc[a][n][i] * sc[n] * wt);
-        }
-    __syncthreads();
-    for (int i = threadIdx.x; i < MM_BM * (MM_BN / 8); i += MM_THREADS) {
-        const int r = i / (MM_BN / 8), ch = i % (MM_BN / 8);
-        const int p = s_pr[r];
-        if (p < NP) *(i32x4*)(ybuf + (size_t)p * H + n0 + ch * 8) = *(const i32x4*)(sY + r * YROW + ch * 8);
-    }
+    multiply(IC<0>{}, nullptr);
+    epilogue(nj - 1);
 }
 
-// ---------------------------------------------------------------- host side
-size_t mfma_gemm1_smem(int H) {
-    return (size_t)MM_ST * MM_STAGE + MM_BM * 4 + 2 * MM_BM * 4 + (size_t)MM_BM * (H / 128);
-}
-size_t mfma_gemm2_smem(int I) { return (size_t)MM_ST * MM_STAGE + 2 * MM_BM * 4 + (size_t)MM_BM * (I / 128); }
+// ------------------------------------------------------------------ host side
+bool mfma_path_ok(int H, int I) { return H % 256 == 0 && I % 128 == 0 && H <= 2048 && I <= 2048 && H >= 256; }
 
-// shapes the two kernels take (the LDS extras grow with H and I)
-bool mfma_path_ok(int H, int I) {
-    return H % MM_BN == 0 && I % 128 == 0 && H <= 8192 && I <= 8192;
+size_t mfma_ws_bytes(int H, int cap) {
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    return up((size_t)(cap / MM_BM) * 8) + 256 + up((size_t)cap * 4) * 2 + up((size_t)cap * (H / 128));
 }
 
-static MPool mpool(const PoolArgs& pa) {
+hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
+                           const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
+                           const int32_t* n_padded, int cap, uint8_t* hq, uint8_t* hs, uint16_t* ybuf, void* ws,
+                           int phase, hipStream_t stream) {
+    const int H = pa.hidden, I = pa.inter;
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    uint8_t* p = (uint8_t*)ws;
+    int2* tiles = (int2*)p;
+    p += up((size_t)(cap / MM_BM) * 8);
+    int* n_tiles = (int*)p;
+    p += 256;
+    int32_t* tokrow = (int32_t*)p;
+    p += up((size_t)cap * 4);
+    float* wsort = (float*)p;
+    p += up((size_t)cap * 4);
+    uint8_t* scl = p;
+
     MPool mp;
     mp.base = (const uint8_t*)pa.base;
     mp.stride = pa.stride;
-    mp.fmt = pa.fmt;
-    for (int f = 0; f < 2; ++f)
-        for (int p = 0; p < 4; ++p) mp.off[f][p] = pa.off[f][p];
-    return mp;
-}
-
-// The 144 KiB of stages exceed the default dynamic LDS limit. The limit is a
-// per-kernel, per-device attribute, so it is set before every launch.
-hipError_t launch_mfma_gemm1(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
-                             const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded, int cap,
-                             int H, int I, uint8_t* hq, uint8_t* hs, hipStream_t stream) {
-    const size_t sm = mfma_gemm1_smem(H);
-    hipError_t e = hipFuncSetAttribute((const void*)gemm1_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sm);
-    if (e != hipSuccess) return e;
-    MOE_LAUNCH(K_GEMM1_FP8, stream, gemm1_mfma_kernel, dim3((cap / MM_BM) * (I / 128)), dim3(MM_THREADS), sm, stream,
-               mpool(pa), xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs);
-    return hipGetLastError();
-}
-
-hipError_t launch_mfma_gemm2(const PoolArgs& pa, int NP, const float* topk_w, const int32_t* sorted_pair,
-                             const int32_t* block_slot, const int32_t* n_padded, int cap, int H, int I,
-                             const uint8_t* hq, const uint8_t* hs, uint16_t* ybuf, hipStream_t stream) {
-    const size_t sm = mfma_gemm2_smem(I);
-    hipError_t e = hipFuncSetAttribute((const void*)gemm2_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sm);
-    if (e != hipSuccess) return e;
-    MOE_LAUNCH(K_GEMM2_FP8, stream, gemm2_mfma_kernel, dim3((cap / MM_BM) * (H / MM_BN)), dim3(MM_THREADS), sm,
-               stream, mpool(pa), NP, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf);
+    for (int i = 0; i < 4; ++i) mp.off[i] = pa.off[0][i];
+    int nwg = device_cus() / 8 * 8;
+    if (nwg < 8) nwg = 8;
+    if (phase == 0) {
+        MOE_LAUNCH(K_MFMA_PREP, stream, mfma_prep_kernel, dim3(1 + (cap + 255) / 256), dim3(256), 0, stream,
+                   sorted_pair, block_slot, pa.fmt, n_padded, NP, k, topk_w, xs, H / 128, tiles, n_tiles, tokrow,
+                   wsort, scl);
+        MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, scl};
+        hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+        if (e != hipSuccess) return e;
+        MOE_LAUNCH(K_GEMM1_FP8, stream, mfma_ffn_kernel<0>, dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream, mp, tl, xq,
+                   NP, H, I, hq, hs, ybuf);
+    } else {
+        MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, hs};
+        hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<1>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+        if (e != hipSuccess) return e;
+        MOE_LAUNCH(K_GEMM2_FP8, stream, mfma_ffn_kernel<1>, dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream, mp, tl, xq,
+                   NP, H, I, hq, hs, ybuf);
+    }
     return hipGetLastError();
 }
 

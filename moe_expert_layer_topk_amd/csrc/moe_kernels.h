@@ -8,7 +8,7 @@ namespace moe {
 
 // kernel ids for launch tracing (names in profile.hip)
 enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
-                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_COMBINE, K_DEQUANT, K_COUNT };
+                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_COUNT };
 void prof_mark(int kid, hipStream_t s, bool start);
 
 // bracket one kernel launch with tracing marks
@@ -59,12 +59,12 @@ hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int 
                               int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream);
 
 bool mfma_path_ok(int H, int I);
-hipError_t launch_mfma_gemm1(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
-                             const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded, int cap,
-                             int H, int I, uint8_t* hq, uint8_t* hs, hipStream_t stream);
-hipError_t launch_mfma_gemm2(const PoolArgs& pa, int NP, const float* topk_w, const int32_t* sorted_pair,
-                             const int32_t* block_slot, const int32_t* n_padded, int cap, int H, int I,
-                             const uint8_t* hq, const uint8_t* hs, uint16_t* ybuf, hipStream_t stream);
+size_t mfma_ws_bytes(int H, int cap);
+// phase 0: prep + gate/up kernel, phase 1: down kernel
+hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
+                           const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
+                           const int32_t* n_padded, int cap, uint8_t* hq, uint8_t* hs, uint16_t* ybuf, void* ws,
+                           int phase, hipStream_t stream);
 
 hipError_t launch_dequant(const PoolArgs& pa, int slot, float* w13, float* w2, hipStream_t stream);
 
