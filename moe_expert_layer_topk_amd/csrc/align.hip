@@ -168,9 +168,16 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
     __shared__ int s_off[MOE_MAX_E];
     __shared__ int s_tmp[2 * ALIGN_WAVES];
     const int e = threadIdx.x;
+    constexpr int B = 8;                 // chunk counts loaded per round trip
     if (e < E) {
         int c = 0;
-        for (int b = 0; b < n_chunks; ++b) c += hist[(size_t)b * E + e];
+        for (int b0 = 0; b0 < n_chunks; b0 += B) {
+            int v[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) v[j] = b0 + j < n_chunks ? hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < B; ++j) c += v[j];
+        }
         s_cnt[e] = c;
     }
     __syncthreads();
@@ -178,10 +185,15 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
                          block_slot, sorted_pair, err);
     if (e < E) {                         // hist[b][e] <- start of chunk b's pairs of expert e
         int run = s_off[e];
-        for (int b = 0; b < n_chunks; ++b) {
-            int c = hist[(size_t)b * E + e];
-            hist[(size_t)b * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < n_chunks; b0 += B) {
+            int v[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) v[j] = b0 + j < n_chunks ? hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (b0 + j < n_chunks) hist[(size_t)(b0 + j) * E + e] = run;
+                run += v[j];
+            }
         }
     }
 }

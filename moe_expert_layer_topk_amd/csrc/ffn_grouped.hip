@@ -41,22 +41,40 @@ __device__ __forceinline__ float2 f16x2_at(const uint8_t* p) {
 }
 
 // ------------------------------------------------------------ activation quant
-// One wave per (row, 128-column group): 2 values per lane.
+// 16 lanes per (row, 128-column group), 8 values (16 bytes) per lane; the
+// group's absolute maximum is a max over the lane's row of 16 (DPP).
 __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                        uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
     const int lane = lane_id();
     const int groups = cols / MOE_ACT_G;
-    const long item = (long)blockIdx.x * 4 + threadIdx.x / MOE_WAVE;
-    if (item >= (long)rows * groups) return;
-    const int r = (int)(item / groups), g = (int)(item % groups);
-    const uint32_t two = *(const uint32_t*)(x + (size_t)r * cols + g * MOE_ACT_G + 2 * lane);
-    const float v0 = bf16_to_f32((uint16_t)(two & 0xFFFF)), v1 = bf16_to_f32((uint16_t)(two >> 16));
-    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const long item = ((long)blockIdx.x * 4 + threadIdx.x / MOE_WAVE) * 4 + lane / 16;
+    const bool live = item < (long)rows * groups;
+    const long it = live ? item : 0;                    // idle lanes redo item 0 and store nothing
+    const int r = (int)(it / groups), g = (int)(it % groups);
+    const size_t off = (size_t)r * cols + g * MOE_ACT_G + 8 * (lane & 15);
+    const i32x4 raw = *(const i32x4*)(x + off);
+    float v[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        v[2 * d] = bf16_to_f32((uint16_t)((uint32_t)raw[d] & 0xFFFF));
+        v[2 * d + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[d] >> 16));
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) amax = fmaxf(amax, fabsf(v[d]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     int s = pow2_exponent_448(amax);
     s = s < -127 ? -127 : (s > 127 ? 127 : s);
-    const uint32_t codes = f32x2_to_e4m3(ldexpf(v0, -s), ldexpf(v1, -s));
-    *(uint16_t*)(xq + (size_t)r * cols + g * MOE_ACT_G + 2 * lane) = (uint16_t)codes;
-    if (lane == 0) xs[(size_t)r * groups + g] = (uint8_t)(s + 127);
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        w[h] = f32x2_to_e4m3(ldexpf(v[4 * h], -s), ldexpf(v[4 * h + 1], -s)) |
+               (f32x2_to_e4m3(ldexpf(v[4 * h + 2], -s), ldexpf(v[4 * h + 3], -s)) << 16);
+    if (live) {
+        *(uint2*)(xq + off) = make_uint2(w[0], w[1]);
+        if ((lane & 15) == 0) xs[(size_t)r * groups + g] = (uint8_t)(s + 127);
+    }
 }
 
 // ------------------------------------------------------------ shared GEMM pieces
@@ -85,13 +103,13 @@ __device__ __forceinline__ void int4_to_e4m3_16(uint2 packed, float zero, uint32
 // Tile: BM pair rows x 128 inter columns (128 gate rows + 128 up rows of W13).
 // Wave w owns inter columns [32w, 32w+32).
 template <int BM>
-__global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t* __restrict__ xq,
-                                                      const uint8_t* __restrict__ xs, int NP, int k,
-                                                      const int32_t* __restrict__ sorted_pair,
-                                                      const int32_t* __restrict__ block_slot,
-                                                      const int32_t* __restrict__ n_padded, int H, int I,
-                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-                                                      int int4_only) {
+__device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __restrict__ xq,
+                                           const uint8_t* __restrict__ xs, int NP, int k,
+                                           const int32_t* __restrict__ sorted_pair,
+                                           const int32_t* __restrict__ block_slot,
+                                           const int32_t* __restrict__ n_padded, int H, int I,
+                                           uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, int int4_only,
+                                           const int mt_idx, const int nt_idx) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* sA = smem;                               // [BM][LDS_ROW]
@@ -101,7 +119,6 @@ __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t
     const int groups = H / MOE_ACT_G;
     float* s_amax = (float*)(s_xs + ((BM * groups + 15) / 16) * 16);   // [4][BM]
 
-    const int mt_idx = blockIdx.y, nt_idx = blockIdx.x;
     if (mt_idx >= *n_padded / BM) return;
     const int slot = block_slot[mt_idx];
     if (slot < 0) return;
@@ -272,17 +289,17 @@ __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t
 // ------------------------------------------------------------ gemm2
 // Tile: BM pair rows x 128 hidden columns; wave w owns columns [32w, 32w+32).
 template <int BM>
-__global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k, const float* __restrict__ topk_w,
-                                                      const int32_t* __restrict__ sorted_pair,
-                                                      const int32_t* __restrict__ block_slot,
-                                                      const int32_t* __restrict__ n_padded, int H, int I,
-                                                      const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-                                                      uint16_t* __restrict__ ybuf, int int4_only) {
+__device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, const float* __restrict__ topk_w,
+                                           const int32_t* __restrict__ sorted_pair,
+                                           const int32_t* __restrict__ block_slot,
+                                           const int32_t* __restrict__ n_padded, int H, int I,
+                                           const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+                                           uint16_t* __restrict__ ybuf, int int4_only, const int mt_idx,
+                                           const int nt_idx) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* sA = smem;                               // [BM][LDS_ROW]
     uint8_t* sB = sA + BM * LDS_ROW;                  // [128][LDS_ROW]
-    const int mt_idx = blockIdx.y, nt_idx = blockIdx.x;
     if (mt_idx >= *n_padded / BM) return;
     const int slot = block_slot[mt_idx];
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
@@ -386,6 +403,52 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
     }
 }
 
+// ------------------------------------------------------------ kernels
+// Grid (column tiles, blocks). With `list`, the workgroups of each column
+// take the listed blocks (count *n_list) in turn instead of block y.
+template <int BM>
+__global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t* __restrict__ xq,
+                                                      const uint8_t* __restrict__ xs, int NP, int k,
+                                                      const int32_t* __restrict__ sorted_pair,
+                                                      const int32_t* __restrict__ block_slot,
+                                                      const int32_t* __restrict__ n_padded, int H, int I,
+                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
+                                                      int int4_only, const int* __restrict__ list,
+                                                      const int* __restrict__ n_list) {
+    if (list == nullptr) {
+        gemm1_tile<BM>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, blockIdx.y,
+                       blockIdx.x);
+        return;
+    }
+    const int n = *n_list;
+    for (int i = blockIdx.y; i < n; i += gridDim.y) {
+        gemm1_tile<BM>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, list[i],
+                       blockIdx.x);
+        __syncthreads();
+    }
+}
+
+template <int BM>
+__global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k, const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ sorted_pair,
+                                                      const int32_t* __restrict__ block_slot,
+                                                      const int32_t* __restrict__ n_padded, int H, int I,
+                                                      const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+                                                      uint16_t* __restrict__ ybuf, int int4_only,
+                                                      const int* __restrict__ list, const int* __restrict__ n_list) {
+    if (list == nullptr) {
+        gemm2_tile<BM>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
+                       blockIdx.y, blockIdx.x);
+        return;
+    }
+    const int n = *n_list;
+    for (int i = blockIdx.y; i < n; i += gridDim.y) {
+        gemm2_tile<BM>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
+                       list[i], blockIdx.x);
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------ host side
 static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -431,29 +494,35 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
                                     const int32_t* n_padded, int cap, int H, int I, uint16_t* out,
                                     hipStream_t stream) {
     const int NP = T * k;
-    const long qitems = (long)T * (H / MOE_ACT_G);
-    MOE_LAUNCH(K_QUANT_ACT, stream, quant_act_kernel, dim3((unsigned)((qitems + 3) / 4)), dim3(256), 0, stream, x, T, H, w.xq, w.xs);
+    const long qitems = (long)T * (H / MOE_ACT_G);      // 16 per block
+    MOE_LAUNCH(K_QUANT_ACT, stream, quant_act_kernel, dim3((unsigned)((qitems + 15) / 16)), dim3(256), 0, stream, x, T, H,
+               w.xq, w.xs);
     dim3 g1((I + 127) / 128, cap / BM);
     size_t sm1 = gemm1_smem<BM>(H);
     dim3 g2(H / 128, cap / BM);
     hipError_t e;
     if (BM == 128 && mfma_path_ok(H, I)) {
         // FP8 blocks on the pipelined kernels; int4 and non-resident blocks on the simple ones
+        // the prep kernel also lists the other blocks (int4 or not resident)
+        const int* olist = nullptr;
+        const int* n_olist = nullptr;
+        mfma_other_list(w.mm, H, cap, &olist, &n_olist);
+        const int oy = cap / BM < 64 ? cap / BM : 64;
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 0, stream);
         if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
-                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1);
+        MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, dim3(g1.x, oy), dim3(GT), sm1, stream, gp, w.xq, w.xs,
+                   NP, k, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1, olist, n_olist);
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 1, stream);
         if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
-                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1);
+        MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, dim3(g2.x, oy), dim3(GT), gemm2_smem<BM>(), stream, gp,
+                   NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1, olist, n_olist);
     } else {
         MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
-                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 0);
+                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 0, nullptr, nullptr);
         MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
-                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 0);
+                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 0, nullptr, nullptr);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -162,28 +162,41 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
                                                        const float* __restrict__ topk_w,
                                                        const uint8_t* __restrict__ xs, int groups,
                                                        int2* __restrict__ tiles, int* __restrict__ n_tiles,
+                                                       int* __restrict__ others, int* __restrict__ n_others,
                                                        int32_t* __restrict__ tokrow, float* __restrict__ wsort,
                                                        uint8_t* __restrict__ scl) {
     const int np = *n_padded;
-    if (blockIdx.x == 0) {
-        __shared__ int s_cnt[4];
+    if (blockIdx.x == 0) {                      // FP8 blocks -> tiles, the rest -> others
+        __shared__ int s_cnt[2][4];
         const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
         const int nb = np / MM_BM;
-        int base = 0;
+        int base = 0, obase = 0;
         for (int b0 = 0; b0 < nb; b0 += 256) {
             const int b = b0 + threadIdx.x;
             const int slot = b < nb ? block_slot[b] : -1;
             const bool f = slot >= 0 && fmt[slot] == 0;
-            const uint64_t bal = __ballot(f);
-            if (lane == 0) s_cnt[wv] = __popcll(bal);
+            const bool o = b < nb && !f;
+            const uint64_t bal = __ballot(f), obal = __ballot(o);
+            if (lane == 0) {
+                s_cnt[0][wv] = __popcll(bal);
+                s_cnt[1][wv] = __popcll(obal);
+            }
             __syncthreads();
-            int off = base;
-            for (int w = 0; w < wv; ++w) off += s_cnt[w];
+            int off = base, ooff = obase;
+            for (int w = 0; w < wv; ++w) {
+                off += s_cnt[0][w];
+                ooff += s_cnt[1][w];
+            }
             if (f) tiles[off + __popcll(bal & lanemask_lt())] = make_int2(b, slot);
-            base += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+            if (o) others[ooff + __popcll(obal & lanemask_lt())] = b;
+            base += s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
+            obase += s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
             __syncthreads();
         }
-        if (threadIdx.x == 0) *n_tiles = base;
+        if (threadIdx.x == 0) {
+            *n_tiles = base;
+            *n_others = obase;
+        }
         return;
     }
     const int pos = (blockIdx.x - 1) * 256 + threadIdx.x;
@@ -439,9 +452,19 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
 // ------------------------------------------------------------------ host side
 bool mfma_path_ok(int H, int I) { return H % 256 == 0 && I % 128 == 0 && H <= 2048 && I <= 2048 && H >= 256; }
 
+// workspace: tiles int2[cap/128], counts (256 B), others int[cap/128], tokrow, wsort, scales
 size_t mfma_ws_bytes(int H, int cap) {
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-    return up((size_t)(cap / MM_BM) * 8) + 256 + up((size_t)cap * 4) * 2 + up((size_t)cap * (H / 128));
+    return up((size_t)(cap / MM_BM) * 8) + 256 + up((size_t)(cap / MM_BM) * 4) + up((size_t)cap * 4) * 2 +
+           up((size_t)cap * (H / 128));
+}
+
+void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_list) {
+    (void)H;
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    uint8_t* p = (uint8_t*)ws + up((size_t)(cap / MM_BM) * 8);
+    *n_list = (const int*)p + 1;
+    *list = (const int*)(p + 256);
 }
 
 hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
@@ -454,7 +477,10 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     int2* tiles = (int2*)p;
     p += up((size_t)(cap / MM_BM) * 8);
     int* n_tiles = (int*)p;
+    int* n_others = n_tiles + 1;
     p += 256;
+    int* others = (int*)p;
+    p += up((size_t)(cap / MM_BM) * 4);
     int32_t* tokrow = (int32_t*)p;
     p += up((size_t)cap * 4);
     float* wsort = (float*)p;
@@ -469,8 +495,8 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     if (nwg < 8) nwg = 8;
     if (phase == 0) {
         MOE_LAUNCH(K_MFMA_PREP, stream, mfma_prep_kernel, dim3(1 + (cap + 255) / 256), dim3(256), 0, stream,
-                   sorted_pair, block_slot, pa.fmt, n_padded, NP, k, topk_w, xs, H / 128, tiles, n_tiles, tokrow,
-                   wsort, scl);
+                   sorted_pair, block_slot, pa.fmt, n_padded, NP, k, topk_w, xs, H / 128, tiles, n_tiles, others,
+                   n_others, tokrow, wsort, scl);
         MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, scl};
         hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);

@@ -60,6 +60,8 @@ hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int 
 
 bool mfma_path_ok(int H, int I);
 size_t mfma_ws_bytes(int H, int cap);
+// blocks the prep kernel found int4 or not resident (device list and count)
+void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_list);
 // phase 0: prep + gate/up kernel, phase 1: down kernel
 hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
                            const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,

@@ -10,50 +10,73 @@
 
 namespace moe {
 
-// Orderable 64-bit key: high word = monotone image of the float (signed zeros
-// merged), low word = 1023 - expert so that a lower id wins ties. 0 = absent.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
+// Orderable 32-bit image of a logit (monotone, signed zeros merged); 0 marks
+// an absent entry and is below the image of every non-NaN float.
+__device__ __forceinline__ uint32_t route_ord(float v) {
     if (v == 0.0f) v = 0.0f;
-    uint32_t u = __float_as_uint(v);
-    uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint32_t)(MOE_MAX_E - 1 - e);
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float route_key_value(uint64_t key) {
-    uint32_t o = (uint32_t)(key >> 32);
-    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(u);
+__device__ __forceinline__ float route_ord_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+    return o > v ? o : v;
+}
+// wave-wide max: row shifts, then row broadcasts; lane 63 ends with the max
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    v = dpp_max_u32<0x111, 0xF>(v);
+    v = dpp_max_u32<0x112, 0xF>(v);
+    v = dpp_max_u32<0x114, 0xF>(v);
+    v = dpp_max_u32<0x118, 0xF>(v);
+    v = dpp_max_u32<0x142, 0xA>(v);
+    v = dpp_max_u32<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Lane r < found returns choice r in (id, weight); lanes >= found return
-// (-1, 0). VPL = logits held per lane (E <= 64 * VPL). Whole wave must call.
+// (-1, 0). VPL = logits held per lane, entry i of lane l is expert 64 i + l
+// (E <= 64 * VPL). Each round takes the largest logit image; among equal
+// images the lowest expert id (lowest i, then lowest lane) wins. Whole wave
+// must call.
 template <int VPL>
 __device__ __forceinline__ int route_token(const float* __restrict__ row, const uint8_t* __restrict__ mask, int E,
                                            int k, int& my_id, float& my_w) {
     const int lane = lane_id();
-    uint64_t key[VPL];
+    uint32_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = i * MOE_WAVE + lane;
         const bool ok = e < E && (mask == nullptr || mask[e] != 0);
-        key[i] = ok ? route_key(row[e], e) : 0ull;
+        key[i] = ok ? route_ord(row[e]) : 0u;
     }
-    float my_logit = 0.f;
+    uint32_t my_ord = 0;
     my_id = -1;
     int found = 0;
     for (int r = 0; r < k; ++r) {
-        uint64_t best = key[0];
+        uint32_t best = key[0];
 #pragma unroll
         for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64_dpp(best);
+        best = wave_max_u32_dpp(best);
         if (best == 0) break;                            // uniform across the wave
+        int sel = -1;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) key[i] = (key[i] == best) ? 0ull : key[i];
+        for (int i = 0; i < VPL; ++i) {
+            const uint64_t b = __ballot(key[i] == best);
+            if (sel < 0 && b != 0) sel = i * MOE_WAVE + (int)__builtin_ctzll(b);
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) key[i] = (i * MOE_WAVE + lane == sel) ? 0u : key[i];
         if (lane == r) {
-            my_logit = route_key_value(best);
-            my_id = MOE_MAX_E - 1 - (int)(uint32_t)(best & 0xFFFFFFFFu);
+            my_ord = best;
+            my_id = sel;
         }
         ++found;
     }
+    const float my_logit = route_ord_value(my_ord);
     const float top = __shfl(my_logit, 0, 64);
     const float z = (lane < found) ? expf(my_logit - top) : 0.f;
     float s = 0.f;
