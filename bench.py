@@ -215,18 +215,34 @@ def main():
     if not args.no_cpu_baseline:
         import oracle  # noqa: F401
         threads = len(os.sched_getaffinity(0))
-        done_tok, t_cpu, n_layers = 0, 0.0, 0
-        sample_tokens = None if T <= 64 else np.arange(min(T, 16))
-        for li, *_ in layers:
-            c0 = time.perf_counter()
-            oracle_layer(li, bank, bm, act, token_subset=sample_tokens)
-            t_cpu += time.perf_counter() - c0
-            done_tok += T if sample_tokens is None else sample_tokens.size
-            n_layers += 1
-            if t_cpu >= args.cpu_seconds:
-                break
-        what = (f"{n_layers} of {L} layers, all {T} tokens each" if sample_tokens is None else
-                f"{n_layers} layers, {sample_tokens.size} of {T} tokens each (route and align run on all)")
+        if T <= 64:
+            # decode sizes: whole layers, as many as fit in the time budget
+            done_tok, t_cpu, n_layers = 0, 0.0, 0
+            for li, *_ in layers:
+                c0 = time.perf_counter()
+                oracle_layer(li, bank, bm, act)
+                t_cpu += time.perf_counter() - c0
+                done_tok += T
+                n_layers += 1
+                if t_cpu >= args.cpu_seconds:
+                    break
+            what = f"{n_layers} of {L} layers, all {T} tokens each"
+        else:
+            # batched sizes: the FFN of a token subset of the first layer (route and
+            # align on all tokens, every routed expert dequantized), the subset
+            # growing 4x until one run takes about a third of the budget
+            li = layers[0][0]
+            n = 16
+            while True:
+                sub = np.arange(min(T, n))
+                c0 = time.perf_counter()
+                oracle_layer(li, bank, bm, act, token_subset=sub)
+                t_cpu = time.perf_counter() - c0
+                if t_cpu >= args.cpu_seconds / 3 or n >= T:
+                    break
+                n *= 4
+            done_tok = sub.size
+            what = f"layer 0, FFN of {sub.size} of {T} tokens (route and align on all {T})"
         cpu = dict(value=round(done_tok / t_cpu, 3), unit="tokens/s", cores=threads, kind="oracle",
                    sample=f"{what}; fp64 NumPy incl. slot dequant; {t_cpu:.1f}s")
         log(f"[bench] cpu oracle {cpu['value']} tokens/s over {t_cpu:.1f}s")

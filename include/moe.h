@@ -164,12 +164,13 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
 int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream);
 
 /* ---------------------------------------------------------------- tracing
- * Launch tracing for measurement (the MOE-GEN explainer, aibr.jp, section 2
- * and its closing checklist, asks for GPU utilisation and throughput figures
- * per module). moe_profile_enable(1) clears old records and brackets every
- * later kernel launch of the library with two HIP events on its stream (not
- * while a stream is being captured); moe_profile_enable(0) stops and frees
- * the events. moe_profile_read() waits for the recorded events of kernel
+ * Launch tracing for measurement (the MOE-GEN explainer, aibr.jp: its
+ * dialogue names throughput and GPU utilisation among the figures to watch).
+ * moe_profile_enable(1) clears old records and makes every later kernel
+ * launch of the library carry a start and a stop HIP event that the dispatch
+ * itself stamps, so a pair spans exactly that kernel's execution (not while
+ * a stream is being captured); moe_profile_enable(0) stops and frees the
+ * events. moe_profile_read() waits for the recorded events of kernel
  * `kernel` (0 <= kernel < moe_profile_kernels(); names from
  * moe_profile_kernel_name) and returns the launch count and the summed
  * milliseconds. Not thread-safe. */

@@ -1,6 +1,7 @@
 // Host-side launch entry points of the gfx950 kernels (internal to libmoe).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -9,14 +10,17 @@ namespace moe {
 // kernel ids for launch tracing (names in profile.hip)
 enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
                 K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_COUNT };
-void prof_mark(int kid, hipStream_t s, bool start);
+// events the next launch of kernel `kid` on `s` should stamp (false: not tracing)
+bool prof_events(int kid, hipStream_t s, hipEvent_t* start, hipEvent_t* stop);
 
-// bracket one kernel launch with tracing marks
-#define MOE_LAUNCH(kid, stream, ...)              \
-    do {                                          \
-        ::moe::prof_mark((kid), (stream), true);  \
-        hipLaunchKernelGGL(__VA_ARGS__);          \
-        ::moe::prof_mark((kid), (stream), false); \
+// launch a kernel; while tracing, its dispatch stamps a start and a stop event
+#define MOE_LAUNCH(kid, stream, kernel, grid, block, shmem, strm, ...)                                   \
+    do {                                                                                                \
+        hipEvent_t moe_ev0_, moe_ev1_;                                                                  \
+        if (::moe::prof_events((kid), (stream), &moe_ev0_, &moe_ev1_))                                  \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, strm, moe_ev0_, moe_ev1_, 0, __VA_ARGS__);  \
+        else                                                                                            \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, strm, __VA_ARGS__);                          \
     } while (0)
 
 struct PoolArgs {

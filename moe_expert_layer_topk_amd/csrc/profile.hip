@@ -1,7 +1,8 @@
-// Launch tracing: when enabled, every kernel the library launches is
-// bracketed by two HIP events on its stream; moe_profile_read() sums the
-// elapsed times per kernel. Off by default; skipped while a stream is being
-// captured into a graph. Single-threaded use.
+// Launch tracing: when enabled, every kernel the library launches carries a
+// start and a stop HIP event that the dispatch itself stamps (AMD's extended
+// launch), so an event pair spans exactly that kernel's execution;
+// moe_profile_read() sums the elapsed times per kernel. Off by default;
+// skipped while a stream is being captured into a graph. Single-threaded use.
 #include "../../include/moe.h"
 #include "moe_kernels.h"
 
@@ -12,8 +13,7 @@ namespace {
 
 struct Mark {
     int kid;
-    bool start;
-    hipEvent_t ev;
+    hipEvent_t start, stop;
 };
 
 bool g_on = false;
@@ -36,23 +36,30 @@ hipEvent_t take_event() {
 }
 
 void recycle() {
-    for (auto& m : g_marks) g_free.push_back(m.ev);
+    for (auto& m : g_marks) {
+        g_free.push_back(m.start);
+        g_free.push_back(m.stop);
+    }
     g_marks.clear();
 }
 
 }  // namespace
 
-void prof_mark(int kid, hipStream_t s, bool start) {
-    if (!g_on) return;
+bool prof_events(int kid, hipStream_t s, hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    if (!g_on) return false;
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone) return;
-    hipEvent_t e = take_event();
-    if (!e) return;
-    if (hipEventRecord(e, s) != hipSuccess) {
-        g_free.push_back(e);
-        return;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
+    hipEvent_t a = take_event(), b = take_event();
+    if (!a || !b) {
+        if (a) g_free.push_back(a);
+        if (b) g_free.push_back(b);
+        return false;
     }
-    g_marks.push_back({kid, start, e});
+    *start = a;
+    *stop = b;
+    g_marks.push_back({kid, a, b});
+    return true;
 }
 
 }  // namespace moe
@@ -79,15 +86,11 @@ int moe_profile_read(int kernel, int* launches, double* total_ms) {
     if (kernel < 0 || kernel >= moe::K_COUNT || !launches || !total_ms) return MOE_EINVAL;
     *launches = 0;
     *total_ms = 0.0;
-    const auto& m = moe::g_marks;
-    for (size_t i = 0; i + 1 < m.size(); ++i) {
-        if (m[i].kid != kernel || !m[i].start) continue;
-        size_t j = i + 1;
-        while (j < m.size() && !(m[j].kid == kernel && !m[j].start)) ++j;
-        if (j == m.size()) break;
-        if (hipEventSynchronize(m[j].ev) != hipSuccess) return MOE_EHIP;
+    for (const auto& m : moe::g_marks) {
+        if (m.kid != kernel) continue;
+        if (hipEventSynchronize(m.stop) != hipSuccess) return MOE_EHIP;
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, m[i].ev, m[j].ev) != hipSuccess) return MOE_EHIP;
+        if (hipEventElapsedTime(&ms, m.start, m.stop) != hipSuccess) return MOE_EHIP;
         *launches += 1;
         *total_ms += ms;
     }
