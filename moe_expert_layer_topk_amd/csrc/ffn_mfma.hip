@@ -25,9 +25,9 @@
 //   row's 16-byte chunks XOR-swizzled by the row index through the source
 //   address of each lane, so that the 16 lanes reading one fragment column
 //   spread over the LDS banks;
-// * 4 waves in a 2 x 2 grid, 64 x 128 outputs each: 32
-//   v_mfma_scale_f32_16x16x128_f8f6f4 per K step, with the power-of-two
-//   activation exponents (E8M0) as the instruction's A scales;
+// * 8 waves in a 4 x 2 grid over a 256 x 256 tile, 64 x 128 outputs each:
+//   32 v_mfma_scale_f32_16x16x128_f8f6f4 per wave and K step, with the
+//   power-of-two activation exponents (E8M0) as the instruction's A scales;
 // * B rows are ordered so that the four accumulators a lane holds for one
 //   row across four fragments are adjacent output columns: epilogue stores
 //   are 4-byte fp8 or 8-byte bf16 runs straight from registers;
@@ -44,16 +44,17 @@
 
 namespace moe {
 
-constexpr int MM_BM = 128;
-constexpr int MM_THREADS = 256;
-constexpr int MM_RING = 3;                              // LDS stages
-constexpr int MM_OPS = (128 + 256) * 128;               // 128 A rows, 256 B rows of 128 bytes
-constexpr int MM_SCL = MM_OPS;                          // 128 row-scale bytes (+128 unused)
+constexpr int MM_BM = 128;                              // rows of an align block
+constexpr int MM_TM = 256;                              // rows of a tile: two blocks of one expert
+constexpr int MM_THREADS = 512;                         // 8 waves: 4 (rows) x 2 (columns)
+constexpr int MM_RING = 2;                              // LDS stages
+constexpr int MM_OPS = (MM_TM + 256) * 128;             // 256 A rows, 256 B rows of 128 bytes
+constexpr int MM_SCL = MM_OPS;                          // 256 row-scale bytes
 constexpr int MM_STAGE = MM_OPS + 256;
-constexpr int MM_META = 2048;                           // per-tile metadata slot
+constexpr int MM_META = 4096;                           // per-tile metadata slot
 constexpr int MM_NMETA = 4;                             // tiles that can be in flight at once
 constexpr int MM_AMAX = MM_RING * MM_STAGE + MM_NMETA * MM_META;
-constexpr int MM_SMEM = MM_AMAX + 2 * MM_BM * 4;
+constexpr int MM_SMEM = MM_AMAX + 2 * MM_TM * 4;
 
 template <int V>
 struct IC {
@@ -67,7 +68,7 @@ struct MPool {
 };
 
 struct MTiles {
-    const int2* tiles;        // (block, slot) of each FP8 block, in order
+    const int4* tiles;        // (first block, slot, blocks (1 or 2), 0) of each FP8 tile, in order
     const int* n_tiles;
     const int32_t* tokrow;    // token of each sorted position (0 for padding)
     const float* wsort;       // route weight of each sorted position (0 for padding)
@@ -87,8 +88,7 @@ __device__ __forceinline__ void wait_vm() {
     case n: wait_vm<n>(); break;
 __device__ __forceinline__ void wait_vm_n(int n) {
     switch (n) {
-        MM_W(0) MM_W(12) MM_W(13) MM_W(14) MM_W(15) MM_W(16) MM_W(24) MM_W(25) MM_W(26) MM_W(27) MM_W(28)
-        MM_W(29) MM_W(30) MM_W(31) MM_W(32)
+        MM_W(0) MM_W(8) MM_W(9) MM_W(10)
         default: wait_vm<0>(); break;
     }
 }
@@ -114,10 +114,10 @@ __device__ __forceinline__ void dma4(const void* src, uint8_t* lds) {
 // with the direct-to-LDS loads in flight (vector memory completes in order),
 // draining the pipeline; scalar loads count on a separate counter.
 typedef int i32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ int2 sload2(const int2* p) {
-    long long r;
-    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
-    return make_int2((int)r, (int)(r >> 32));
+__device__ __forceinline__ int4 sload4(const int4* p) {
+    i32x4 r;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return make_int4(r[0], r[1], r[2], r[3]);
 }
 __device__ __forceinline__ i32x16 sload16(const int32_t* p) {
     i32x16 r;
@@ -152,33 +152,48 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 __device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------ prep
-// Block 0 lists, in order, the blocks whose slot is resident and FP8; the
-// other blocks write, per sorted position, the token, the route weight and
-// the token's activation scale bytes transposed to [block][K step][row].
+// Block 0 lists, in order, the FP8 tiles (pairs of consecutive blocks of one
+// resident FP8 expert, counted from the start of the expert's segment; an odd
+// last block makes a one-block tile) and the other blocks (int4 or not
+// resident); the other workgroups write, per sorted position, the token, the
+// route weight and the token's activation scale bytes transposed to
+// [block][K step][row].
 __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restrict__ sorted_pair,
                                                        const int32_t* __restrict__ block_slot,
                                                        const uint8_t* __restrict__ fmt,
                                                        const int32_t* __restrict__ n_padded, int NP, int k,
                                                        const float* __restrict__ topk_w,
                                                        const uint8_t* __restrict__ xs, int groups,
-                                                       int2* __restrict__ tiles, int* __restrict__ n_tiles,
+                                                       int4* __restrict__ tiles, int* __restrict__ n_tiles,
                                                        int* __restrict__ others, int* __restrict__ n_others,
                                                        int32_t* __restrict__ tokrow, float* __restrict__ wsort,
                                                        uint8_t* __restrict__ scl) {
     const int np = *n_padded;
-    if (blockIdx.x == 0) {                      // FP8 blocks -> tiles, the rest -> others
+    if (blockIdx.x == 0) {
         __shared__ int s_cnt[2][4];
+        __shared__ int s_last[4];
         const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
         const int nb = np / MM_BM;
-        int base = 0, obase = 0;
+        int base = 0, obase = 0, carry = 0;     // carry: last segment start before this chunk
         for (int b0 = 0; b0 < nb; b0 += 256) {
             const int b = b0 + threadIdx.x;
-            const int slot = b < nb ? block_slot[b] : -1;
-            const bool f = slot >= 0 && fmt[slot] == 0;
-            const bool o = b < nb && !f;
-            const uint64_t bal = __ballot(f), obal = __ballot(o);
+            const bool valid = b < nb;
+            const int slot = valid ? block_slot[b] : -1;
+            const bool start = valid && (b == 0 || block_slot[b - 1] != slot);
+            const uint64_t smask = __ballot(start);
+            const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+            if (lane == 0) s_last[wv] = smask ? b0 + 64 * wv + 63 - __clzll(smask) : -1;
+            __syncthreads();
+            int seg = carry;
+            for (int w = 0; w < wv; ++w) seg = s_last[w] > seg ? s_last[w] : seg;
+            if (smask & upto) seg = b0 + 64 * wv + 63 - __clzll(smask & upto);
+            const bool f = valid && slot >= 0 && fmt[slot] == 0;
+            const bool t = f && ((b - seg) & 1) == 0;
+            const bool o = valid && !f;
+            const int nblk = (t && b + 1 < nb && block_slot[b + 1] == slot) ? 2 : 1;
+            const uint64_t tbal = __ballot(t), obal = __ballot(o);
             if (lane == 0) {
-                s_cnt[0][wv] = __popcll(bal);
+                s_cnt[0][wv] = __popcll(tbal);
                 s_cnt[1][wv] = __popcll(obal);
             }
             __syncthreads();
@@ -187,10 +202,11 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
                 off += s_cnt[0][w];
                 ooff += s_cnt[1][w];
             }
-            if (f) tiles[off + __popcll(bal & lanemask_lt())] = make_int2(b, slot);
+            if (t) tiles[off + __popcll(tbal & lanemask_lt())] = make_int4(b, slot, nblk, 0);
             if (o) others[ooff + __popcll(obal & lanemask_lt())] = b;
             base += s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
             obase += s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
+            for (int w = 0; w < 4; ++w) carry = s_last[w] > carry ? s_last[w] : carry;
             __syncthreads();
         }
         if (threadIdx.x == 0) {
@@ -212,18 +228,22 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
 }
 
 // ------------------------------------------------------------------ gemm kernels
-// KIND 0: gate/up (gemm1), KIND 1: down (gemm2).
+// KIND 0: gate/up (gemm1), KIND 1: down (gemm2). A tile is 256 rows (two
+// blocks; in a one-block tile the second half repeats the first block's rows
+// and its results are dropped) by 256 B rows (KIND 0: 128 gate + the matching
+// 128 up rows of W13 = 128 columns of h; KIND 1: 256 rows of W2).
 template <int KIND>
 __global__ void __launch_bounds__(MM_THREADS, 1)
-    mfma_ffn_kernel(MPool pool, MTiles tl, const uint8_t* __restrict__ xq, int NP, int H, int I,
+    mfma_ffn_kernel(MPool pool, MTiles tl, const uint8_t* __restrict__ xq, int NP, int H, int I_arg,
                     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ ybuf) {
+    const int I = I_arg;
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
     const int m = lane & 15, q = lane >> 4;
-    const int mw = wv & 1, nw = wv >> 1;
+    const int mw = wv & 3, nw = wv >> 2;                  // 64-row group, 128-column half
     const int S = KIND == 0 ? H / 128 : I / 128;          // K steps per tile
-    const int NT = KIND == 0 ? I / 128 : H / 256;         // column tiles per block
+    const int NT = KIND == 0 ? I / 128 : H / 256;         // column tiles per block pair
     const int hgroups = I / 128;
 
     // this workgroup's tiles: start + idx + per_x * j, j < nj
@@ -236,89 +256,94 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     if (nj == 0) return;
     const int N = nj * S;
 
-    // metadata loads of this wave per tile (256-byte dword loads) and their LDS offset
-    const int meta_n = KIND == 0 ? (wv == 1 || wv == 2 ? 2 : 0) : (wv == 1 || wv == 2 ? 2 : (wv == 3 ? 4 : 0));
-    const int meta_off = KIND == 0 ? (wv == 2 ? 512 : 0) : (wv == 2 ? 512 : (wv == 3 ? 1024 : 0));
+    // metadata dword loads (256 B each) of this wave per tile, into the tile's
+    // metadata slot at byte meta_off. KIND 0: wave 1 gate, wave 2 up row scales
+    // of the 128 columns; KIND 1: waves 1, 2 pair ids of the two blocks, waves
+    // 3, 4 their route weights, waves 5, 6 the W2 row scales of the 256 columns.
+    const int meta_n = KIND == 0 ? (wv == 1 || wv == 2 ? 2 : 0) : (wv >= 1 && wv <= 6 ? 2 : 0);
+    const int meta_off = KIND == 0 ? (wv == 2 ? 512 : 0) : (wv - 1) * 512;
 
-    // ---- issue side: sources of the tile being loaded. Wave w loads A rows
-    // 32 w + 8 j + i / 8 (j < 4) and B rows 64 w + 8 j + i / 8 (j < 8); lane i
-    // puts the source chunk cs = (i % 8) ^ (i / 8) of its row at chunk i % 8.
+    // ---- issue side: sources of the tile being loaded. Wave w loads A and B
+    // rows 32 w + 8 j + i / 8 (j < 4); lane i puts the source chunk
+    // (i % 8) ^ (i / 8) of its row at chunk i % 8.
     const int csw = 16 * ((lane & 7) ^ (lane >> 3));
-    const uint8_t* pA[4];
-    const uint8_t* pB0 = nullptr;         // B row of j = 0; row of j is + (32 (j & 1) + (j >> 1)) rows
-    const uint8_t* pS = nullptr;          // row-scale bytes (wave 0)
-    const uint8_t* pM = nullptr;          // metadata (meta_n > 0)
-    // B stage row 64 w + 8 j + i / 8 = fragment 4 w + j / 2, fragment row 8 (j & 1) + i / 8;
+    // wave-uniform bases plus 32-bit per-lane offsets (fewer live registers)
+    const uint8_t* bA = KIND == 0 ? xq : hq;
+    const uint8_t* bB = nullptr;          // B rows of this tile
+    const uint8_t* bS = nullptr;          // row-scale bytes of this tile (wave 0)
+    const uint8_t* bM = nullptr;          // metadata source (meta_n > 0)
+    uint32_t oA[4], oB = 0, oS = 0, oM = 0;   // B row of j is oB + (32 (j & 1) + (j >> 1)) rows
+    // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
     // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
     // (KIND 0: n / 4 picks gate or up rows, CW = 64; KIND 1: CW = 128)
-    const int brow0 = (KIND == 0 ? (wv & 1) * I + (wv >> 1) * 64 : (wv >> 1) * 128 + (wv & 1) * 64) + 4 * (lane >> 3);
+    const int brow0 = (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 : (wv >> 2) * 128 + ((wv & 3) >> 1) * 64) +
+                      2 * (wv & 1) + 4 * (lane >> 3);
     auto setup = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
-        const int2 d = sload2(tl.tiles + L / NT);
-        const int mt = d.x, nt = L % NT;
+        const int4 d = sload4(tl.tiles + L / NT);
+        const int b = d.x, nt = L % NT, two = d.z == 2;
         const uint8_t* sb = pool.base + (size_t)d.y * pool.stride;
-        pS = tl.scl + (size_t)mt * S * MM_BM + 4 * (lane & 31);
+        const int blk_w = b + ((wv >> 2) & two);            // block of this wave's A rows
+        const int r_w = 32 * (wv & 3);                      // first of them inside the block
+        bS = tl.scl + (size_t)b * S * MM_BM;
+        oS = ((lane >> 5) & two) * S * MM_BM + 4 * (lane & 31);
         if (KIND == 0) {
-            // tokens of rows 32 wv .. 32 wv + 31, scalar loads
-            const i32x16 ta = sload16(tl.tokrow + mt * MM_BM + 32 * wv);
-            const i32x16 tb = sload16(tl.tokrow + mt * MM_BM + 32 * wv + 16);
+            const int32_t* tr = tl.tokrow + blk_w * MM_BM + r_w;   // 32 tokens, scalar loads
+            const i32x16 t0 = sload16(tr), t1 = sload16(tr + 16);
             const int r8 = lane >> 3;
             int t[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                t[0] = r8 == r ? ta[r] : t[0];
-                t[1] = r8 == r ? ta[8 + r] : t[1];
-                t[2] = r8 == r ? tb[r] : t[2];
-                t[3] = r8 == r ? tb[8 + r] : t[3];
+                t[0] = r8 == r ? t0[r] : t[0];
+                t[1] = r8 == r ? t0[8 + r] : t[1];
+                t[2] = r8 == r ? t1[r] : t[2];
+                t[3] = r8 == r ? t1[8 + r] : t[3];
             }
 #pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2) pA[j2] = xq + (size_t)t[j2] * H + csw;
+            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)t[j2] * H + csw;
             const int c0 = nt * 128;
-            pB0 = sb + pool.off[0] + (size_t)(brow0 + c0) * H + csw;
-            const float* s13 = (const float*)(sb + pool.off[1]);
-            pM = (const uint8_t*)(s13 + (wv == 2 ? I : 0) + c0 + lane);
+            bB = sb + pool.off[0] + (size_t)c0 * H;
+            oB = (uint32_t)brow0 * H + csw;
+            bM = sb + pool.off[1] + 4 * ((wv == 2 ? I : 0) + c0);
+            oM = 4 * lane;
         } else {
-#pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2)
-                pA[j2] = hq + (size_t)(mt * MM_BM + 32 * wv + 8 * j2 + (lane >> 3)) * I + csw;
+            bA = hq + (size_t)(blk_w * MM_BM + r_w) * I;
+            oA[0] = (uint32_t)(lane >> 3) * I + csw;        // row 8 j is + 8 j I (added at issue)
             const int n0 = nt * 256;
-            pB0 = sb + pool.off[2] + (size_t)(brow0 + n0) * I + csw;
-            if (wv == 1) pM = (const uint8_t*)(tl.sorted_pair + mt * MM_BM + lane);
-            else if (wv == 2) pM = (const uint8_t*)(tl.wsort + mt * MM_BM + lane);
-            else pM = (const uint8_t*)((const float*)(sb + pool.off[3]) + n0 + lane);
+            bB = sb + pool.off[2] + (size_t)n0 * I;
+            oB = (uint32_t)brow0 * I + csw;
+            const int half = (wv - 1) & 1;                  // waves 1..6: first or second half
+            if (wv == 1 || wv == 2) bM = (const uint8_t*)(tl.sorted_pair + (b + (half & two)) * MM_BM);
+            else if (wv == 3 || wv == 4) bM = (const uint8_t*)(tl.wsort + (b + (half & two)) * MM_BM);
+            else bM = sb + pool.off[3] + 4 * (n0 + 128 * half);
+            oM = 4 * lane;
         }
     };
     // vector memory operations stage s puts in flight for this wave
-    auto stage_ops = [&](int s) __attribute__((always_inline)) { return 12 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n : 0); };
-    // The k-th load of stage s for this wave: A rows (k < 4), B rows (k < 12),
-    // then the row scales (wave 0) and, on a tile's first stage, metadata.
-    auto issue_one = [&](int s, int k) __attribute__((always_inline)) {
+    auto stage_ops = [&](int s) __attribute__((always_inline)) {
+        return 8 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n : 0);
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
         const int g = s % S;
+        if (g == 0) setup(s / S);
         uint8_t* st = smem + (s % MM_RING) * MM_STAGE;
         const int k0 = g * 128;
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
-        if (k < 4) {
-            dma16(pA[k] + k0, st + (32 * wv + 8 * k) * 128);
-        } else if (k < 12) {
-            const int j2 = k - 4;
-            dma16(pB0 + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0, st + MM_BM * 128 + (64 * wv + 8 * j2) * 128);
-        } else if (wv == 0) {
-            if (k == 12) dma4(pS + g * MM_BM, st + MM_SCL);
-        } else if (g == 0 && k - 12 < meta_n) {
-            uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
-            dma4(pM + 256 * (k - 12), md + 256 * (k - 12));
-        }
-    };
-    auto issue = [&](int s) __attribute__((always_inline)) {
-        if (s % S == 0) setup(s / S);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) issue_one(s, k);
+        for (int j2 = 0; j2 < 4; ++j2)
+            dma16(bA + (KIND == 0 ? oA[j2] : oA[0] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2)
+            dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + oB, st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
+        if (wv == 0) dma4(bS + g * MM_BM + oS, st + MM_SCL);
+        if (g == 0) {
+            uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
+            for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + oM, md + 256 * h);
+        }
     };
 
     // ---- compute side
     f32x4 acc[4][8];
-    i32x8 FA[4], FB[8];
-    int SA[4];
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -326,32 +351,30 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
             for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
     const int o0 = ((2 * q) ^ (m & 7)) << 4, o1 = ((2 * q + 1) ^ (m & 7)) << 4;
-    auto read_a = [&](const uint8_t* st, int a) __attribute__((always_inline)) {
-        FA[a] = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
-        SA[a] = st[MM_SCL + 64 * mw + 16 * a + m];
-    };
-    auto read_b = [&](const uint8_t* st, int n) __attribute__((always_inline)) {
-        FB[n] = frag_read(st + MM_BM * 128, 16 * (8 * nw + n) + m, o0, o1);
-    };
-    // Multiply the fragments in registers; when `next` is set, refill each
-    // fragment register from stage `next` once its last use has been issued.
-    // Multiply the fragments in registers; with `refill`, reload each
-    // fragment register from stage `next` once its last use has been issued.
-    auto multiply = [&](auto refill, const uint8_t* next) __attribute__((always_inline)) {
-        constexpr bool R = decltype(refill)::value != 0;
+    // one K step from LDS: the 8 B fragments stay in registers, the A
+    // fragments are read one 16-row group at a time
+    auto multiply = [&](const uint8_t* st) __attribute__((always_inline)) {
+        i32x8 FB[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) FB[n] = frag_read(st + MM_TM * 128, 16 * (8 * nw + n) + m, o0, o1);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            const i32x8 FA = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
+            const int sa = st[MM_SCL + 64 * mw + 16 * a + m];
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
-                if (R && a == 3) read_b(next, n);
-            }
-            if (R) read_a(next, a);
+            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(FA, FB[n], acc[a][n], sa, 127);
         }
     };
     auto epilogue = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
-        const int mt = sload2(tl.tiles + L / NT).x, nt = L % NT;
+        const int4 d = sload4(tl.tiles + L / NT);
+        const int b = d.x, nt = L % NT, rows = d.z * MM_BM;
+        // opaque copies: row addresses are formed here, not hoisted out of the
+        // step loop into registers the loop would then have to spill
+        int I = I_arg, ln = lane;
+        asm volatile("" : "+s"(I));
+        asm volatile("" : "+v"(ln));
+        const int m = ln & 15, q = ln >> 4;
         const uint8_t* md = smem + MM_RING * MM_STAGE + (j % MM_NMETA) * MM_META;
         if (KIND == 0) {
             float* s_amax = (float*)(smem + MM_AMAX);
@@ -370,7 +393,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                         mx = fmaxf(mx, fabsf(h));
                     }
                     mx = row16_max(mx);
-                    if (m == 0) s_amax[nw * MM_BM + 64 * mw + 16 * a + 4 * q + i] = mx;
+                    if (m == 0) s_amax[nw * MM_TM + 64 * mw + 16 * a + 4 * q + i] = mx;
                 }
             barrier_lds();
             const int c = nt * 128 + nw * 64 + 4 * m;
@@ -379,18 +402,21 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 64 * mw + 16 * a + 4 * q + i;
-                    int e = pow2_exponent_448(fmaxf(s_amax[row], s_amax[MM_BM + row]));
+                    int e = pow2_exponent_448(fmaxf(s_amax[row], s_amax[MM_TM + row]));
                     e = e < -127 ? -127 : (e > 127 ? 127 : e);
                     const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
                     const uint32_t hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
-                    *(uint32_t*)(hq + (size_t)(mt * MM_BM + row) * I + c) = lo | (hi << 16);
-                    if (nw == 0 && m == 0) hs[((size_t)mt * hgroups + nt) * MM_BM + row] = (uint8_t)(e + 127);
+                    if (row < rows) {
+                        *(uint32_t*)(hq + (size_t)(b * MM_BM + row) * I + c) = lo | (hi << 16);
+                        if (nw == 0 && m == 0)
+                            hs[((size_t)(b + row / MM_BM) * hgroups + nt) * MM_BM + row % MM_BM] = (uint8_t)(e + 127);
+                    }
                 }
         } else {
             const int32_t* s_pr = (const int32_t*)md;
-            const float* s_w = (const float*)(md + 512);
-            const f32x4 sc0 = *(const f32x4*)(md + 1024 + 4 * (nw * 128 + 4 * m));
-            const f32x4 sc1 = *(const f32x4*)(md + 1024 + 4 * (nw * 128 + 64 + 4 * m));
+            const float* s_w = (const float*)(md + 1024);
+            const f32x4 sc0 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 4 * m));
+            const f32x4 sc1 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 64 + 4 * m));
             const int c = nt * 256 + nw * 128 + 4 * m;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -408,7 +434,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                         v[2 * h] = bf16x2_rne(y0, y1);
                         v[2 * h + 1] = bf16x2_rne(y2, y3);
                     }
-                    if (p < NP) {
+                    if (row < rows && p < NP) {
                         uint16_t* yr = ybuf + (size_t)p * H + c;
                         *(uint2*)yr = make_uint2(v[0], v[1]);
                         *(uint2*)(yr + 64) = make_uint2(v[2], v[3]);
@@ -417,52 +443,43 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         }
     };
 
-    // ---- the stream of K steps
+    // ---- the stream of K steps. Step s sits in LDS buffer s % 2: while step
+    // cs is multiplied, step cs+1 is in flight; once every wave is done with
+    // buffer cs % 2 it is refilled with step cs+2 (before the epilogue, so the
+    // next tile's loads overlap it).
     zero_acc();
     int is = 0;
     for (; is < MM_RING && is < N; ++is) issue(is);
-    {
-        int after = 0;                                  // issued after stage 0
-        for (int s = 1; s < is; ++s) after += stage_ops(s);
-        wait_vm_n(after);
-        barrier_lds();
-        const uint8_t* st = smem;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) read_b(st, n);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) read_a(st, a);
-    }
-    for (int cs = 0; cs + 1 < N; ++cs) {
-        wait_vm_n(cs + 2 < is ? stage_ops(cs + 2) : 0);   // stage cs+1 landed
-        barrier_lds();                                  // ... for every wave; stage cs's buffer is free
+    for (int cs = 0; cs < N; ++cs) {
+        wait_vm_n(cs + 1 < is ? stage_ops(cs + 1) : 0);   // step cs landed
+        barrier_lds();                                  // ... for every wave
+        multiply(smem + (cs % MM_RING) * MM_STAGE);
         if (is < N) {
+            barrier_lds();                              // every wave is done with buffer cs % 2
             issue(is);
             ++is;
         }
-        multiply(IC<1>{}, smem + ((cs + 1) % MM_RING) * MM_STAGE);
         if (cs % S == S - 1) {
             epilogue(cs / S);
             zero_acc();
         }
     }
-    multiply(IC<0>{}, nullptr);
-    epilogue(nj - 1);
 }
 
 // ------------------------------------------------------------------ host side
 bool mfma_path_ok(int H, int I) { return H % 256 == 0 && I % 128 == 0 && H <= 2048 && I <= 2048 && H >= 256; }
 
-// workspace: tiles int2[cap/128], counts (256 B), others int[cap/128], tokrow, wsort, scales
+// workspace: tiles int4[cap/128], counts (256 B), others int[cap/128], tokrow, wsort, scales
 size_t mfma_ws_bytes(int H, int cap) {
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-    return up((size_t)(cap / MM_BM) * 8) + 256 + up((size_t)(cap / MM_BM) * 4) + up((size_t)cap * 4) * 2 +
+    return up((size_t)(cap / MM_BM) * 16) + 256 + up((size_t)(cap / MM_BM) * 4) + up((size_t)cap * 4) * 2 +
            up((size_t)cap * (H / 128));
 }
 
 void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_list) {
     (void)H;
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-    uint8_t* p = (uint8_t*)ws + up((size_t)(cap / MM_BM) * 8);
+    uint8_t* p = (uint8_t*)ws + up((size_t)(cap / MM_BM) * 16);
     *n_list = (const int*)p + 1;
     *list = (const int*)(p + 256);
 }
@@ -474,8 +491,8 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     const int H = pa.hidden, I = pa.inter;
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
     uint8_t* p = (uint8_t*)ws;
-    int2* tiles = (int2*)p;
-    p += up((size_t)(cap / MM_BM) * 8);
+    int4* tiles = (int4*)p;
+    p += up((size_t)(cap / MM_BM) * 16);
     int* n_tiles = (int*)p;
     int* n_others = n_tiles + 1;
     p += 256;
