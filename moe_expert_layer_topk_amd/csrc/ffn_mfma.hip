@@ -15,11 +15,12 @@
 //   tiles; the workgroups of one XCD (blocks are dealt round-robin over the 8
 //   XCDs) take consecutive tiles, so the same token rows and the same
 //   expert's weights are shared in that XCD's L2;
-// * the K steps of all tiles of a workgroup form one stream: a ring of three
-//   LDS stages is filled by direct-to-LDS 16-byte loads; while step s is
-//   multiplied from registers, the fragments of step s+1 are read from LDS
-//   and steps s+2 and s+3 are in flight, also across tile boundaries, so the
-//   next tile's loads hide behind the current tile's last steps and epilogue;
+// * the K steps of all tiles of a workgroup form one stream through two LDS
+//   buffers filled by direct-to-LDS 16-byte loads: a step is read into
+//   registers, its buffer is refilled two steps ahead, and the step is
+//   multiplied from registers while the next two are in flight, also across
+//   tile boundaries, so the next tile's loads hide behind the current tile's
+//   last steps and epilogue;
 // * a stage holds 128 A rows and 256 B rows of 128 bytes; one 16-byte load
 //   instruction fills 8 whole rows (full 128-byte lines from memory), each
 //   row's 16-byte chunks XOR-swizzled by the row index through the source
@@ -351,19 +352,24 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
             for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
     const int o0 = ((2 * q) ^ (m & 7)) << 4, o1 = ((2 * q + 1) ^ (m & 7)) << 4;
-    // one K step from LDS: the 8 B fragments stay in registers, the A
-    // fragments are read one 16-row group at a time
-    auto multiply = [&](const uint8_t* st) __attribute__((always_inline)) {
-        i32x8 FB[8];
+    // one K step: every fragment of the step is read into registers first, so
+    // the LDS buffer can be refilled while the matrix instructions run
+    i32x8 FA[4], FB[8];
+    int SA[4];
+    auto read_step = [&](const uint8_t* st) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) FB[n] = frag_read(st + MM_TM * 128, 16 * (8 * nw + n) + m, o0, o1);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const i32x8 FA = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
-            const int sa = st[MM_SCL + 64 * mw + 16 * a + m];
-#pragma unroll
-            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(FA, FB[n], acc[a][n], sa, 127);
+            FA[a] = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
+            SA[a] = st[MM_SCL + 64 * mw + 16 * a + m];
         }
+    };
+    auto multiply = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
     };
     auto epilogue = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
@@ -443,22 +449,23 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         }
     };
 
-    // ---- the stream of K steps. Step s sits in LDS buffer s % 2: while step
-    // cs is multiplied, step cs+1 is in flight; once every wave is done with
-    // buffer cs % 2 it is refilled with step cs+2 (before the epilogue, so the
-    // next tile's loads overlap it).
+    // ---- the stream of K steps. Step s sits in LDS buffer s % 2. Step cs is
+    // read into registers, then (once every wave has read it) its buffer is
+    // refilled with step cs+2 while step cs is multiplied: steps cs+1 and
+    // cs+2 are in flight during the matrix work and the epilogue.
     zero_acc();
     int is = 0;
     for (; is < MM_RING && is < N; ++is) issue(is);
     for (int cs = 0; cs < N; ++cs) {
         wait_vm_n(cs + 1 < is ? stage_ops(cs + 1) : 0);   // step cs landed
         barrier_lds();                                  // ... for every wave
-        multiply(smem + (cs % MM_RING) * MM_STAGE);
+        read_step(smem + (cs % MM_RING) * MM_STAGE);
         if (is < N) {
-            barrier_lds();                              // every wave is done with buffer cs % 2
+            barrier_lds();                              // every wave has read step cs
             issue(is);
             ++is;
         }
+        multiply();
         if (cs % S == S - 1) {
             epilogue(cs / S);
             zero_acc();
