@@ -23,9 +23,11 @@
 //   last steps and epilogue;
 // * a stage holds 128 A rows and 256 B rows of 128 bytes; one 16-byte load
 //   instruction fills 8 whole rows (full 128-byte lines from memory), each
-//   row's 16-byte chunks XOR-swizzled by the row index through the source
-//   address of each lane, so that the 16 lanes reading one fragment column
-//   spread over the LDS banks;
+//   row's 16-byte chunks XOR-swizzled through the source address of each
+//   lane: chunk c of stage row r sits at c ^ f(r % 16), f(m) = (m / 2) & 5,
+//   a placement measured free of LDS bank conflicts for 16-byte fragment
+//   reads (rows m of a fragment at lanes m + 16 q, chunk 2q or 2q+1), where
+//   the row-index XOR by r % 8 loses half the LDS bandwidth;
 // * 8 waves in a 4 x 2 grid over a 256 x 256 tile, 64 x 128 outputs each:
 //   32 v_mfma_scale_f32_16x16x128_f8f6f4 per wave and K step, with the
 //   power-of-two activation exponents (E8M0) as the instruction's A scales;
@@ -128,7 +130,7 @@ __device__ __forceinline__ i32x16 sload16(const int32_t* p) {
 
 // 32 codes of stage row r for the lane group q (K bytes [32 q, 32 q + 32)):
 // o0, o1 are the lane's swizzled offsets of chunks 2q and 2q+1 (rows read by
-// a lane all share r % 8 = m % 8)
+// a lane all share r % 16 = m)
 __device__ __forceinline__ i32x8 frag_read(const uint8_t* st, int r, int o0, int o1) {
     const i32x4 lo = *(const i32x4*)(st + r * 128 + o0);
     const i32x4 hi = *(const i32x4*)(st + r * 128 + o1);
@@ -265,15 +267,17 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     const int meta_off = KIND == 0 ? (wv == 2 ? 512 : 0) : (wv - 1) * 512;
 
     // ---- issue side: sources of the tile being loaded. Wave w loads A and B
-    // rows 32 w + 8 j + i / 8 (j < 4); lane i puts the source chunk
-    // (i % 8) ^ (i / 8) of its row at chunk i % 8.
-    const int csw = 16 * ((lane & 7) ^ (lane >> 3));
+    // rows r = 32 w + 8 j + i / 8 (j < 4); lane i puts the source chunk
+    // (i % 8) ^ f(r % 16) of its row at chunk i % 8, f(r % 16) = ((i / 16) & 1)
+    // | 4 (j & 1).
+    const int csw0 = 16 * ((lane & 7) ^ ((lane >> 4) & 1));        // loads j even
+    const int csw1 = 16 * ((lane & 7) ^ (4 | ((lane >> 4) & 1)));  // loads j odd
     // wave-uniform bases plus 32-bit per-lane offsets (fewer live registers)
     const uint8_t* bA = KIND == 0 ? xq : hq;
     const uint8_t* bB = nullptr;          // B rows of this tile
     const uint8_t* bS = nullptr;          // row-scale bytes of this tile (wave 0)
     const uint8_t* bM = nullptr;          // metadata source (meta_n > 0)
-    uint32_t oA[4], oB = 0, oS = 0, oM = 0;   // B row of j is oB + (32 (j & 1) + (j >> 1)) rows
+    uint32_t oA[4], oB0 = 0, oB1 = 0, oS = 0, oM = 0;   // B row of j: oB(j & 1) + (32 (j & 1) + (j >> 1)) rows
     // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
     // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
     // (KIND 0: n / 4 picks gate or up rows, CW = 64; KIND 1: CW = 128)
@@ -301,18 +305,21 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                 t[3] = r8 == r ? t1[8 + r] : t[3];
             }
 #pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)t[j2] * H + csw;
+            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)t[j2] * H + ((j2 & 1) ? csw1 : csw0);
             const int c0 = nt * 128;
             bB = sb + pool.off[0] + (size_t)c0 * H;
-            oB = (uint32_t)brow0 * H + csw;
+            oB0 = (uint32_t)brow0 * H + csw0;
+            oB1 = (uint32_t)brow0 * H + csw1;
             bM = sb + pool.off[1] + 4 * ((wv == 2 ? I : 0) + c0);
             oM = 4 * lane;
         } else {
             bA = hq + (size_t)(blk_w * MM_BM + r_w) * I;
-            oA[0] = (uint32_t)(lane >> 3) * I + csw;        // row 8 j is + 8 j I (added at issue)
+            oA[0] = (uint32_t)(lane >> 3) * I + csw0;       // row 8 j is + 8 j I (added at issue)
+            oA[1] = (uint32_t)(lane >> 3) * I + csw1;
             const int n0 = nt * 256;
             bB = sb + pool.off[2] + (size_t)n0 * I;
-            oB = (uint32_t)brow0 * I + csw;
+            oB0 = (uint32_t)brow0 * I + csw0;
+            oB1 = (uint32_t)brow0 * I + csw1;
             const int half = (wv - 1) & 1;                  // waves 1..6: first or second half
             if (wv == 1 || wv == 2) bM = (const uint8_t*)(tl.sorted_pair + (b + (half & two)) * MM_BM);
             else if (wv == 3 || wv == 4) bM = (const uint8_t*)(tl.wsort + (b + (half & two)) * MM_BM);
@@ -332,10 +339,10 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2)
-            dma16(bA + (KIND == 0 ? oA[j2] : oA[0] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
+            dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2)
-            dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + oB, st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
+            dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0), st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
         if (wv == 0) dma4(bS + g * MM_BM + oS, st + MM_SCL);
         if (g == 0) {
             uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
@@ -351,7 +358,8 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
 #pragma unroll
             for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
-    const int o0 = ((2 * q) ^ (m & 7)) << 4, o1 = ((2 * q + 1) ^ (m & 7)) << 4;
+    const int fm = (m >> 1) & 5;
+    const int o0 = ((2 * q) ^ fm) << 4, o1 = ((2 * q + 1) ^ fm) << 4;
     // one K step: every fragment of the step is read into registers first, so
     // the LDS buffer can be refilled while the matrix instructions run
     i32x8 FA[4], FB[8];
