@@ -17,8 +17,10 @@
 //   expert's weights are shared in that XCD's L2;
 // * the K steps of all tiles of a workgroup form one stream through two LDS
 //   buffers filled by direct-to-LDS 16-byte loads: a step is read into
-//   registers, its buffer is refilled two steps ahead, and the step is
-//   multiplied from registers while the next two are in flight, also across
+//   registers, its buffer is refilled two steps ahead by loads issued
+//   between the step's matrix instructions (so the CU's load path and the
+//   matrix pipe work at the same time), and the step is multiplied from
+//   registers while the next two are in flight, also across
 //   tile boundaries, so the next tile's loads hide behind the current tile's
 //   last steps and epilogue;
 // * a stage holds 128 A rows and 256 B rows of 128 bytes; one 16-byte load
@@ -331,23 +333,40 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     auto stage_ops = [&](int s) __attribute__((always_inline)) {
         return 8 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n : 0);
     };
-    auto issue = [&](int s) __attribute__((always_inline)) {
-        const int g = s % S;
-        if (g == 0) setup(s / S);
-        uint8_t* st = smem + (s % MM_RING) * MM_STAGE;
-        const int k0 = g * 128;
+    // the loads of step s into LDS buffer u (u = s % 2, except past the end of
+    // the stream, where the last step is loaded again into the buffer the
+    // current step left, so the loop needs no branch around them)
+    auto dma_a = [&](int s, int u, int j2) __attribute__((always_inline)) {
+        uint8_t* st = smem + u * MM_STAGE;
+        const int k0 = (s % S) * 128;
+        dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
+    };
+    auto dma_b = [&](int s, int u, int j2) __attribute__((always_inline)) {
+        uint8_t* st = smem + u * MM_STAGE;
+        const int k0 = (s % S) * 128;
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
-#pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2)
-            dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
-#pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2)
-            dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0), st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
-        if (wv == 0) dma4(bS + g * MM_BM + oS, st + MM_SCL);
+        dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0), st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
+    };
+    auto dma_tail = [&](int s, int u) __attribute__((always_inline)) {
+        uint8_t* st = smem + u * MM_STAGE;
+        const int g = s % S;
+        // opaque copies: the 64-bit addresses are formed here, not kept live
+        uint32_t os = oS, om = oM;
+        asm volatile("" : "+v"(os));
+        asm volatile("" : "+v"(om));
+        if (wv == 0) dma4(bS + g * MM_BM + os, st + MM_SCL);
         if (g == 0) {
             uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
-            for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + oM, md + 256 * h);
+            for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + om, md + 256 * h);
         }
+    };
+    auto issue = [&](int s, int u) __attribute__((always_inline)) {
+        if (s % S == 0) setup(s / S);
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) dma_a(s, u, j2);
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) dma_b(s, u, j2);
+        dma_tail(s, u);
     };
 
     // ---- compute side
@@ -373,11 +392,23 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
             SA[a] = st[MM_SCL + 64 * mw + 16 * a + m];
         }
     };
-    auto multiply = [&]() __attribute__((always_inline)) {
+    // the matrix instructions of one K step with the 16-byte loads of step s
+    // between them: a load instruction waits while the CU's load path is
+    // busy, and the matrix pipe keeps working on the instructions issued
+    // before it
+    auto multiply_issue = [&](int s, int u) __attribute__((always_inline)) {
+        dma_tail(s, u);                                 // branches: kept out of the sequence below
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+            for (int n = 0; n < 8; ++n) {
+                acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+                const int k = 8 * a + n;
+                if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
+                if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
     };
     auto epilogue = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
@@ -459,26 +490,27 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
 
     // ---- the stream of K steps. Step s sits in LDS buffer s % 2. Step cs is
     // read into registers, then (once every wave has read it) its buffer is
-    // refilled with step cs+2 while step cs is multiplied: steps cs+1 and
-    // cs+2 are in flight during the matrix work and the epilogue.
+    // refilled with step cs+2, the loads issued between the matrix
+    // instructions of step cs: steps cs+1 and cs+2 are in flight during the
+    // matrix work and the epilogue.
     zero_acc();
-    int is = 0;
-    for (; is < MM_RING && is < N; ++is) issue(is);
+    issue(0, 0);
+    issue(min(1, N - 1), 1);
     for (int cs = 0; cs < N; ++cs) {
-        wait_vm_n(cs + 1 < is ? stage_ops(cs + 1) : 0);   // step cs landed
+        wait_vm_n(stage_ops(min(cs + 1, N - 1)));       // step cs landed
         barrier_lds();                                  // ... for every wave
         read_step(smem + (cs % MM_RING) * MM_STAGE);
-        if (is < N) {
-            barrier_lds();                              // every wave has read step cs
-            issue(is);
-            ++is;
-        }
-        multiply();
+        barrier_lds();                                  // every wave has read step cs
+        __builtin_amdgcn_sched_barrier(0);
+        const int s2 = min(cs + 2, N - 1);
+        if (cs + 2 < N && s2 % S == 0) setup(s2 / S);
+        multiply_issue(s2, cs % MM_RING);
         if (cs % S == S - 1) {
             epilogue(cs / S);
             zero_acc();
         }
     }
+    wait_vm<0>();      // no load into LDS outlives the workgroup
 }
 
 // ------------------------------------------------------------------ host side
