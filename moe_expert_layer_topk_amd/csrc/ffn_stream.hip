@@ -77,6 +77,12 @@ __device__ __forceinline__ float2 half2_at(const uint8_t* p) {
     return make_float2((float)h[0], (float)h[1]);
 }
 
+// Workgroup barrier that waits only for the wave's LDS traffic: the fence of
+// __syncthreads() would also wait for every global load in flight.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 constexpr int G_THREADS = 256;
 constexpr int G_WAVES = 4;
 constexpr int ROWS = 16;      // inter rows (gate and up each) per gemm1 unit
@@ -275,6 +281,13 @@ constexpr int P1_MAXB = 16;      // blocks per workgroup range the LDS tables ho
 struct P1W { i32x4 v[P1_G][2]; f32x4 s; };   // [group][chunk] of this lane's row + scales of rows 4q..4q+3
 struct P1X { i32x4 v[P1_G][2][2]; };         // [group][chunk][half] of this lane's token row
 
+// An empty use of a register set: the compiler waits for its loads here.
+__device__ __forceinline__ void p1_landed(const P1W& W) {
+#pragma unroll
+    for (int j = 0; j < P1_G; ++j) asm volatile("" ::"v"(W.v[j][0]), "v"(W.v[j][1]));
+    asm volatile("" ::"v"(W.s));
+}
+
 // A-tile row of lane m: gate row i0 + m (m < 8) or up row I + i0 + m - 8
 __device__ __forceinline__ int p1_row(int i0, int m, int I) { return m < 8 ? i0 + m : I + i0 + m - 8; }
 
@@ -287,28 +300,25 @@ __device__ __forceinline__ void p1_issue_w(P1W& W, const SlotView& pool, int slo
     const uint8_t* wr = sb + (size_t)p1_row(i0, m, I) * H;
 #pragma unroll
     for (int j = 0; j < P1_G; ++j) {
-        const int g = wv + j * G_WAVES;
-        if (g < groups) {
+        // no branch (the compiler's load counting would turn conservative at
+        // the join): groups past the row repeat its last group, unused
+        const int g = min(wv + j * G_WAVES, groups - 1);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) W.v[j][c] = *(const i32x4*)(wr + g * 128 + c * 64 + q * 16);
-        }
+        for (int c = 0; c < 2; ++c) W.v[j][c] = *(const i32x4*)(wr + g * 128 + c * 64 + q * 16);
     }
 }
 
-__device__ __forceinline__ void p1_issue_x(P1X& X, const uint16_t* xr, bool valid, int q, int wv, int groups) {
+// Token row of this lane (row 0 for a padding lane: its output column is
+// never stored); no branches, as in p1_issue_w.
+__device__ __forceinline__ void p1_issue_x(P1X& X, const uint16_t* xr, int q, int wv, int groups) {
 #pragma unroll
     for (int j = 0; j < P1_G; ++j) {
-        const int g = wv + j * G_WAVES;
+        const int g = min(wv + j * G_WAVES, groups - 1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int k0 = g * 128 + c * 64 + q * 16;
-            if (g < groups && valid) {
-                X.v[j][c][0] = *(const i32x4*)(xr + k0);
-                X.v[j][c][1] = *(const i32x4*)(xr + k0 + 8);
-            } else {
-                X.v[j][c][0] = i32x4{0, 0, 0, 0};
-                X.v[j][c][1] = i32x4{0, 0, 0, 0};
-            }
+            X.v[j][c][0] = *(const i32x4*)(xr + k0);
+            X.v[j][c][1] = *(const i32x4*)(xr + k0 + 8);
         }
     }
 }
@@ -364,7 +374,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     SlotView pool, int n_slots, const uint16_t* __restrict__ x, int NP, int k,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
     const int32_t* __restrict__ n_padded, int H, int I, uint16_t* __restrict__ hbuf) {
-    __shared__ f32x4 s_red[G_WAVES][MOE_WAVE];
+    __shared__ f32x4 s_red[2][G_WAVES][MOE_WAVE];     // unit u uses half u % 2
     __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
     __shared__ int s_slot[P1_MAXB];
     __shared__ int s_pr[P1_MAXB][16];
@@ -378,24 +388,37 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     const int u_end = min(n_units, u_begin + per);
     const int b_first = u_begin / ntile;
     const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
-    // ---- descriptors of my blocks and the format tags: one round trip
-    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
-    for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
+    if (nblk == 0) return;
+    P1W WA, WB;
+    P1X X;
+    int xblock = -1;
+    // ---- the descriptors of my blocks and the format tags, and the first
+    // unit's weights, in one round trip. Loads complete in issue order, so the
+    // descriptor loads go first; the weights are loaded in the FP8 layout
+    // before the slot's format is known (an int4 slot is at least as large,
+    // so the loads stay inside it, and its unit ignores them).
+    const int i0f = threadIdx.x;
+    const int bb0 = i0f / 17, r0 = i0f % 17;
+    uint8_t f0 = 0;
+    int d0 = 0;
+    if (i0f < n_slots) f0 = pool.fmt[i0f];
+    if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
+    __builtin_amdgcn_sched_barrier(0);              // keep the descriptor loads ahead of the weights
+    p1_issue_w(WA, pool, max(block_slot[b_first], 0), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i0f < n_slots) s_fmt[i0f] = f0;
+    if (i0f < nblk * 17) {
+        if (r0 == 16) s_slot[bb0] = d0;
+        else s_pr[bb0][r0] = d0;
+    }
+    for (int i = i0f + G_THREADS; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+    for (int i = i0f + G_THREADS; i < nblk * 17; i += G_THREADS) {
         const int bb = i / 17, r = i % 17;
         if (r == 16) s_slot[bb] = block_slot[b_first + bb];
         else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
     }
-    __syncthreads();
-    if (nblk == 0) return;
+    barrier_lds();                                   // tables written; the weight loads stay in flight
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
-
-    P1W WA, WB;
-    P1X X;
-    int xblock = -1;
-    {
-        const int s0 = s_slot[0];
-        if (s0 >= 0 && fmt_of(s0) == 0) p1_issue_w(WA, pool, s0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
-    }
     auto step = [&](int u, P1W& Wc, P1W& Wn) {
         const int bb = u / ntile - b_first;
         const int i0 = (u % ntile) * P1_ROWS;
@@ -404,15 +427,19 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != xblock) {              // new block: its token rows, before the prefetch
-            p1_issue_x(X, x + (size_t)(valid ? pr / k : 0) * H, valid, q, wv, groups);
+            p1_issue_x(X, x + (size_t)(valid ? pr / k : 0) * H, q, wv, groups);
             xblock = bb;
         }
-        if (u + 1 < u_end) {
-            const int bn = (u + 1) / ntile - b_first;
-            const int sn = s_slot[bn];
-            if (sn >= 0 && fmt_of(sn) == 0)
-                p1_issue_w(Wn, pool, sn, ((u + 1) % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        {
+            // the next unit's weights (FP8 layout, also for an int4 or absent
+            // slot, whose unit ignores them; past the range: this unit again)
+            const int un = min(u + 1, u_end - 1);
+            const int sn = max(s_slot[un / ntile - b_first], 0);
+            p1_issue_w(Wn, pool, sn, (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
+        // every path waits here for this unit's weight loads, so no load into
+        // a register set is still pending when the set is refilled
+        p1_landed(Wc);
         if (slot < 0) return;                          // uniform over the workgroup
         f32x4 acc;
         if (fmt == 0) {
@@ -420,12 +447,12 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         } else {
             acc = p1_int4(pool, slot, X, i0, m, q, wv, H, I, groups);
         }
-        s_red[wv][lane] = acc;
-        __syncthreads();
+        s_red[u & 1][wv][lane] = acc;
+        barrier_lds();
         if (wv == 0) {
-            f32x4 v = s_red[0][lane];
+            f32x4 v = s_red[u & 1][0][lane];
 #pragma unroll
-            for (int w2 = 1; w2 < G_WAVES; ++w2) v += s_red[w2][lane];
+            for (int w2 = 1; w2 < G_WAVES; ++w2) v += s_red[u & 1][w2][lane];
             // lanes q = 0, 1 hold gate rows, q = 2, 3 the up rows of the same inter index
             f32x4 o;
 #pragma unroll
@@ -438,7 +465,9 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
                     make_uint2(two_bf16(hv[0], hv[1]), two_bf16(hv[2], hv[3]));
             }
         }
-        __syncthreads();
+        // no barrier here: unit u+1 writes the other half of s_red, and unit
+        // u+2 writes this half only after the barrier of unit u+1, which wave
+        // 0 reaches after its reads above
     };
     for (int u = u_begin; u < u_end; u += 2) {
         step(u, WA, WB);
