@@ -272,8 +272,6 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     // rows r = 32 w + 8 j + i / 8 (j < 4); lane i puts the source chunk
     // (i % 8) ^ f(r % 16) of its row at chunk i % 8, f(r % 16) = ((i / 16) & 1)
     // | 4 (j & 1).
-    const int csw0 = 16 * ((lane & 7) ^ ((lane >> 4) & 1));        // loads j even
-    const int csw1 = 16 * ((lane & 7) ^ (4 | ((lane >> 4) & 1)));  // loads j odd
     // wave-uniform bases plus 32-bit per-lane offsets (fewer live registers)
     const uint8_t* bA = KIND == 0 ? xq : hq;
     const uint8_t* bB = nullptr;          // B rows of this tile
@@ -283,9 +281,15 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
     // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
     // (KIND 0: n / 4 picks gate or up rows, CW = 64; KIND 1: CW = 128)
-    const int brow0 = (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 : (wv >> 2) * 128 + ((wv & 3) >> 1) * 64) +
-                      2 * (wv & 1) + 4 * (lane >> 3);
     auto setup = [&](int j) __attribute__((always_inline)) {
+        // per-lane constants formed here from an opaque copy of the lane id,
+        // not held in registers across the step loop
+        int lane = lane_id();
+        asm volatile("" : "+v"(lane));
+        const int csw0 = 16 * ((lane & 7) ^ ((lane >> 4) & 1));        // loads j even
+        const int csw1 = 16 * ((lane & 7) ^ (4 | ((lane >> 4) & 1)));  // loads j odd
+        const int brow0 = (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 : (wv >> 2) * 128 + ((wv & 3) >> 1) * 64) +
+                          2 * (wv & 1) + 4 * (lane >> 3);
         const int L = start + idx + per_x * j;
         const int4 d = sload4(tl.tiles + L / NT);
         const int b = d.x, nt = L % NT, two = d.z == 2;
