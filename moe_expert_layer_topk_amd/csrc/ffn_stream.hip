@@ -278,45 +278,58 @@ constexpr int P1_G = 4;          // 128-wide K groups per wave (hidden <= 2048)
 constexpr int P1_ROWS = 8;       // inter rows per unit (gate and up each)
 constexpr int P1_MAXB = 16;      // blocks per workgroup range the LDS tables hold
 
-struct P1W { i32x4 v[P1_G][2]; f32x4 s; };   // [group][chunk] of this lane's row + scales of rows 4q..4q+3
+// A unit's weights in registers, in one of two layouts (nine 16-byte loads
+// either way, with no branch between them, so the compiler's count of loads
+// in flight stays exact):
+// * FP8 slot: r[2 j + c] = 16 codes of this lane's row, K group g = wv + 4 j,
+//   bytes [g 128 + c 64 + q 16, +16); r[8] = fp32 row scales of the C rows
+//   4q..4q+3.
+// * int4 slot: r[j] = 32 nibbles of this lane's row, K group g = 4 wv + j,
+//   elements [g 128 + q 32, +32); r[4] = (scale, zero) of the row for groups
+//   4 wv .. 4 wv + 3; r[5..8] repeat r[4] (unused).
+// The token rows of a block are loaded in the matching K order (p1_issue_x).
+struct P1W { i32x4 r[9]; };
 struct P1X { i32x4 v[P1_G][2][2]; };         // [group][chunk][half] of this lane's token row
 
 // An empty use of a register set: the compiler waits for its loads here.
 __device__ __forceinline__ void p1_landed(const P1W& W) {
 #pragma unroll
-    for (int j = 0; j < P1_G; ++j) asm volatile("" ::"v"(W.v[j][0]), "v"(W.v[j][1]));
-    asm volatile("" ::"v"(W.s));
+    for (int i = 0; i < 9; ++i) asm volatile("" ::"v"(W.r[i]));
 }
 
 // A-tile row of lane m: gate row i0 + m (m < 8) or up row I + i0 + m - 8
 __device__ __forceinline__ int p1_row(int i0, int m, int I) { return m < 8 ? i0 + m : I + i0 + m - 8; }
 
-__device__ __forceinline__ void p1_issue_w(P1W& W, const SlotView& pool, int slot, int i0, int m, int q, int wv,
-                                           int H, int I, int groups) {
+__device__ __forceinline__ void p1_issue_w(P1W& W, const SlotView& pool, int slot, int fmt, int i0, int m, int q,
+                                           int wv, int H, int I, int groups) {
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const float* s13 = (const float*)(sb + pool.off[0][1]);
-    // C rows 4q..4q+3: q = 0, 1 gate rows i0 + 4q..; q = 2, 3 up rows i0 + 4(q-2)..
-    W.s = *(const f32x4*)(s13 + (q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2)));
-    const uint8_t* wr = sb + (size_t)p1_row(i0, m, I) * H;
+    const int row = p1_row(i0, m, I);
+    // FP8 sources (groups past the row repeat its last group, unused)
+    const uint8_t* wr8 = sb + (size_t)row * H;
+    const uint8_t* sc8 = sb + pool.off[0][1] + 4 * (q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2));
+    // int4 sources
+    const uint8_t* wr4 = sb + pool.off[1][0] + (size_t)row * (H / 2) + q * 16;
+    const uint8_t* sz4 = sb + pool.off[1][1] + ((size_t)row * groups + min(4 * wv, groups - 1)) * 4;
 #pragma unroll
-    for (int j = 0; j < P1_G; ++j) {
-        // no branch (the compiler's load counting would turn conservative at
-        // the join): groups past the row repeat its last group, unused
-        const int g = min(wv + j * G_WAVES, groups - 1);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) W.v[j][c] = *(const i32x4*)(wr + g * 128 + c * 64 + q * 16);
+    for (int i = 0; i < 8; ++i) {
+        const int j = i >> 1, c = i & 1;
+        const uint8_t* p8 = wr8 + min(wv + j * G_WAVES, groups - 1) * 128 + c * 64 + q * 16;
+        const uint8_t* p4 = i < 4 ? wr4 + min(4 * wv + i, groups - 1) * 64 : sz4;
+        W.r[i] = *(const i32x4*)(fmt ? p4 : p8);
     }
+    W.r[8] = *(const i32x4*)(fmt ? sz4 : sc8);
 }
 
 // Token row of this lane (row 0 for a padding lane: its output column is
-// never stored); no branches, as in p1_issue_w.
-__device__ __forceinline__ void p1_issue_x(P1X& X, const uint16_t* xr, int q, int wv, int groups) {
+// never stored) in the K order of the block's weight layout; no branches.
+__device__ __forceinline__ void p1_issue_x(P1X& X, const uint16_t* xr, int fmt, int q, int wv, int groups) {
 #pragma unroll
     for (int j = 0; j < P1_G; ++j) {
-        const int g = min(wv + j * G_WAVES, groups - 1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int k0 = g * 128 + c * 64 + q * 16;
+            const int k8 = min(wv + j * G_WAVES, groups - 1) * 128 + c * 64 + q * 16;
+            const int k4 = min(4 * wv + j, groups - 1) * 128 + q * 32 + c * 16;
+            const int k0 = fmt ? k4 : k8;
             X.v[j][c][0] = *(const i32x4*)(xr + k0);
             X.v[j][c][1] = *(const i32x4*)(xr + k0 + 8);
         }
@@ -331,41 +344,39 @@ __device__ __forceinline__ f32x4 p1_mma(const P1W& W, const P1X& X, int wv, int 
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             bf16x8 a0, a1, xb0, xb1;
-            fp8x16_to_bf16(W.v[j][c], a0, a1);
+            fp8x16_to_bf16(W.r[2 * j + c], a0, a1);
             split_bf16(X.v[j][c][0], X.v[j][c][1], xb0, xb1);
             acc = mfma_bf16_16x16x32(a0, xb0, acc);
             acc = mfma_bf16_16x16x32(a1, xb1, acc);
         }
     }
-    return acc;
+    return acc * __builtin_bit_cast(f32x4, W.r[8]);
 }
 
-// int4 unit, synchronous: rows as in p1_row, this wave's groups, scales applied
-__device__ __forceinline__ f32x4 p1_int4(const SlotView& pool, int slot, const P1X& X, int i0, int m, int q, int wv,
-                                         int H, int I, int groups) {
-    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int row = p1_row(i0, m, I);
-    const uint8_t* wr = sb + (size_t)row * (H / 2);
-    const uint8_t* sz = sb + pool.off[1][1];
-    const int orow = q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2);     // first C row this lane holds
+// int4 unit: (q - z) exactly in bf16 before the matrix instructions, each
+// group's scale after them; the scales of C rows 4q..4q+3 come from the
+// lanes that loaded those rows.
+__device__ __forceinline__ f32x4 p1_int4_mma(const P1W& W, const P1X& X, int q, int wv, int groups) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < P1_G; ++j) {
-        const int g = wv + j * G_WAVES;
-        if (g >= groups) break;
-        const float z = half2_at(sz + ((size_t)row * groups + g) * 4).y;
+        if (4 * wv + j >= groups) break;              // uniform over the wave
+        const uint32_t sz = (uint32_t)W.r[4][j];      // (scale, zero) of this lane's row, group 4 wv + j
+        const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
         f32x4 t4 = {0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint2 rw = *(const uint2*)(wr + (g * 128 + c * 64 + q * 16) / 2);
             bf16x8 a0, a1, xb0, xb1;
-            int4x16_to_bf16(rw, z, a0, a1);
+            int4x16_to_bf16(make_uint2((uint32_t)W.r[j][2 * c], (uint32_t)W.r[j][2 * c + 1]), z, a0, a1);
             split_bf16(X.v[j][c][0], X.v[j][c][1], xb0, xb1);
             t4 = mfma_bf16_16x16x32(a0, xb0, t4);
             t4 = mfma_bf16_16x16x32(a1, xb1, t4);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += half2_at(sz + ((size_t)(orow + i) * groups + g) * 4).x * t4[i];
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t szr = (uint32_t)__shfl((int)sz, 4 * q + i, 64);
+            acc[i] += (float)__builtin_bit_cast(_Float16, (uint16_t)(szr & 0xFFFFu)) * t4[i];
+        }
     }
     return acc;
 }
@@ -404,7 +415,11 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     if (i0f < n_slots) f0 = pool.fmt[i0f];
     if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
     __builtin_amdgcn_sched_barrier(0);              // keep the descriptor loads ahead of the weights
-    p1_issue_w(WA, pool, max(block_slot[b_first], 0), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    {
+        const int s0 = max(block_slot[b_first], 0);
+        const int f0 = (pool.fmt[s0] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+        p1_issue_w(WA, pool, s0, f0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (i0f < n_slots) s_fmt[i0f] = f0;
     if (i0f < nblk * 17) {
@@ -427,7 +442,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != xblock) {              // new block: its token rows, before the prefetch
-            p1_issue_x(X, x + (size_t)(valid ? pr / k : 0) * H, q, wv, groups);
+            p1_issue_x(X, x + (size_t)(valid ? pr / k : 0) * H, fmt, q, wv, groups);
             xblock = bb;
         }
         {
@@ -435,18 +450,15 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             // slot, whose unit ignores them; past the range: this unit again)
             const int un = min(u + 1, u_end - 1);
             const int sn = max(s_slot[un / ntile - b_first], 0);
-            p1_issue_w(Wn, pool, sn, (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+            p1_issue_w(Wn, pool, sn, fmt_of(sn), (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
         // every path waits here for this unit's weight loads, so no load into
         // a register set is still pending when the set is refilled
         p1_landed(Wc);
         if (slot < 0) return;                          // uniform over the workgroup
         f32x4 acc;
-        if (fmt == 0) {
-            acc = p1_mma(Wc, X, wv, groups) * Wc.s;
-        } else {
-            acc = p1_int4(pool, slot, X, i0, m, q, wv, H, I, groups);
-        }
+        if (fmt == 0) acc = p1_mma(Wc, X, wv, groups);
+        else acc = p1_int4_mma(Wc, X, q, wv, groups);
         s_red[u & 1][wv][lane] = acc;
         barrier_lds();
         if (wv == 0) {
