@@ -631,25 +631,47 @@ constexpr int P2_MAXB = 16;
 
 constexpr int P2_C = 8;          // 64-wide K chunks per wave (inter <= 512)
 
-struct P2W { i32x4 v[P2_C]; f32x4 s; };
+// A unit's W2 rows in registers, as in gemm1's P1W (nine 16-byte loads in
+// either layout):
+// * FP8 slot: r[c] = 16 codes of this lane's row, bytes [c 64 + q 16, +16);
+//   r[8] = fp32 row scales of the C rows 4q..4q+3.
+// * int4 slot: r[g] = 32 nibbles of this lane's row, K group g, elements
+//   [g 128 + q 32, +32) (g < 4); r[4] = (scale, zero) of the row for groups
+//   0..3; r[5..8] repeat r[4] (unused).
+struct P2W { i32x4 r[9]; };
 struct P2H { i32x4 v[P2_C][2]; };
 
-__device__ __forceinline__ void p2_issue_w(P2W& W, const SlotView& pool, int slot, int n0, int m, int q, int I,
-                                           int chunks) {
-    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    W.s = *(const f32x4*)((const float*)(sb + pool.off[0][3]) + n0 + 4 * q);
-    const uint8_t* wr = sb + pool.off[0][2] + (size_t)(n0 + m) * I;
+__device__ __forceinline__ void p2_landed(const P2W& W) {
 #pragma unroll
-    for (int c = 0; c < P2_C; ++c)
-        if (c < chunks) W.v[c] = *(const i32x4*)(wr + c * 64 + q * 16);
+    for (int i = 0; i < 9; ++i) asm volatile("" ::"v"(W.r[i]));
 }
 
-__device__ __forceinline__ void p2_issue_h(P2H& Hh, const uint16_t* hr, bool valid, int q, int chunks) {
+__device__ __forceinline__ void p2_issue_w(P2W& W, const SlotView& pool, int slot, int fmt, int n0, int m, int q,
+                                           int I, int chunks) {
+    const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
+    const int groups = I / MOE_INT4_G;
+    const uint8_t* wr8 = sb + pool.off[0][2] + (size_t)(n0 + m) * I + q * 16;
+    const uint8_t* sc8 = sb + pool.off[0][3] + 4 * (n0 + 4 * q);
+    const uint8_t* wr4 = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2) + q * 16;
+    const uint8_t* sz4 = sb + pool.off[1][3] + (size_t)(n0 + m) * groups * 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint8_t* p8 = wr8 + min(i, chunks - 1) * 64;
+        const uint8_t* p4 = i < 4 ? wr4 + min(i, max(groups, 1) - 1) * 64 : sz4;
+        W.r[i] = *(const i32x4*)(fmt ? p4 : p8);
+    }
+    W.r[8] = *(const i32x4*)(fmt ? sz4 : sc8);
+}
+
+// h row of this lane's position in the K order of the block's W2 layout
+// (zero for a padding position)
+__device__ __forceinline__ void p2_issue_h(P2H& Hh, const uint16_t* hr, bool valid, int fmt, int q, int chunks) {
 #pragma unroll
     for (int c = 0; c < P2_C; ++c) {
+        const int k0 = fmt ? (c >> 1) * 128 + q * 32 + (c & 1) * 16 : c * 64 + q * 16;
         if (c < chunks && valid) {
-            Hh.v[c][0] = *(const i32x4*)(hr + c * 64 + q * 16);
-            Hh.v[c][1] = *(const i32x4*)(hr + c * 64 + q * 16 + 8);
+            Hh.v[c][0] = *(const i32x4*)(hr + k0);
+            Hh.v[c][1] = *(const i32x4*)(hr + k0 + 8);
         } else {
             Hh.v[c][0] = i32x4{0, 0, 0, 0};
             Hh.v[c][1] = i32x4{0, 0, 0, 0};
@@ -691,7 +713,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     float wt = 0.f;
     {
         const int s0 = s_slot[0];
-        if (s0 >= 0 && fmt_of(s0) == 0) p2_issue_w(WA, pool, s0, (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        if (s0 >= 0) p2_issue_w(WA, pool, s0, fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
     }
     auto step = [&](int u, P2W& Wc, P2W& Wn) {
         const int bb = u / ntile - b_first;
@@ -700,14 +722,13 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != hblock) {              // new block: its h rows and route weights
-            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + m) * I, valid, q, chunks);
+            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + m) * I, valid, fmt_of(slot), q, chunks);
             wt = valid ? topk_w[pr] : 0.f;
             hblock = bb;
         }
         if (u + 1 < u_end) {
             const int sn = s_slot[(u + 1) / ntile - b_first];
-            if (sn >= 0 && fmt_of(sn) == 0)
-                p2_issue_w(Wn, pool, sn, ((u + 1) % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+            if (sn >= 0) p2_issue_w(Wn, pool, sn, fmt_of(sn), ((u + 1) % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
         }
         float* yrow = ybuf + (size_t)(valid ? pr : 0) * H + n0 + 4 * q;
         if (slot < 0) {                               // non-resident expert: its pairs add zero
@@ -720,33 +741,36 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
             for (int c = 0; c < P2_C; ++c) {
                 if (c >= chunks) break;                // uniform
                 bf16x8 a0, a1, h0, h1;
-                fp8x16_to_bf16(Wc.v[c], a0, a1);
+                fp8x16_to_bf16(Wc.r[c], a0, a1);
                 split_bf16(Hh.v[c][0], Hh.v[c][1], h0, h1);
                 acc = mfma_bf16_16x16x32(a0, h0, acc);
                 acc = mfma_bf16_16x16x32(a1, h1, acc);
             }
-            acc *= Wc.s;
+            acc *= __builtin_bit_cast(f32x4, Wc.r[8]);
         } else {
-            const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-            const uint8_t* wr = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2);
-            const uint8_t* sz = sb + pool.off[1][3];
+            // (q - z) exactly in bf16, each group's scale after its matrix
+            // instructions; the scales of C rows 4q..4q+3 from the lanes that
+            // loaded those rows
 #pragma unroll
             for (int g = 0; g < P2_C / 2; ++g) {
                 if (g >= groups) break;                // uniform
-                const float z = half2_at(sz + ((size_t)(n0 + m) * groups + g) * 4).y;
+                const uint32_t sz = (uint32_t)Wc.r[4][g];
+                const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
                 f32x4 t4 = {0, 0, 0, 0};
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
                     const int c = g * 2 + c2;
-                    const uint2 rw = *(const uint2*)(wr + (c * 64 + q * 16) / 2);
                     bf16x8 a0, a1, h0, h1;
-                    int4x16_to_bf16(rw, z, a0, a1);
+                    int4x16_to_bf16(make_uint2((uint32_t)Wc.r[g][2 * c2], (uint32_t)Wc.r[g][2 * c2 + 1]), z, a0, a1);
                     split_bf16(Hh.v[c][0], Hh.v[c][1], h0, h1);
                     t4 = mfma_bf16_16x16x32(a0, h0, t4);
                     t4 = mfma_bf16_16x16x32(a1, h1, t4);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += half2_at(sz + ((size_t)(n0 + 4 * q + i) * groups + g) * 4).x * t4[i];
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t szr = (uint32_t)__shfl((int)sz, 4 * q + i, 64);
+                    acc[i] += (float)__builtin_bit_cast(_Float16, (uint16_t)(szr & 0xFFFFu)) * t4[i];
+                }
             }
         }
         if (valid) *(f32x4*)yrow = acc * wt;
