@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     // unit's weights, in one round trip. Loads complete in issue order, so the
     // descriptor loads go first; the weights are loaded in the FP8 layout
     // before the slot's format is known (an int4 slot is at least as large,
-    // so the loads stay inside it, and its unit ignores them).
+    // so the loads stay inside it) and loaded again if the slot is int4.
     const int i0f = threadIdx.x;
     const int bb0 = i0f / 17, r0 = i0f % 17;
     uint8_t f0 = 0;
@@ -415,11 +415,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     if (i0f < n_slots) f0 = pool.fmt[i0f];
     if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
     __builtin_amdgcn_sched_barrier(0);              // keep the descriptor loads ahead of the weights
-    {
-        const int s0 = max(block_slot[b_first], 0);
-        const int f0 = (pool.fmt[s0] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
-        p1_issue_w(WA, pool, s0, f0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
-    }
+    p1_issue_w(WA, pool, max(block_slot[b_first], 0), 0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
     __builtin_amdgcn_sched_barrier(0);
     if (i0f < n_slots) s_fmt[i0f] = f0;
     if (i0f < nblk * 17) {
@@ -434,6 +430,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     }
     barrier_lds();                                   // tables written; the weight loads stay in flight
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
+    if (fmt_of(s_slot[0]) == 1) {                    // the first unit is int4: load it in its own layout
+        p1_landed(WA);
+        p1_issue_w(WA, pool, s_slot[0], 1, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    }
     auto step = [&](int u, P1W& Wc, P1W& Wn) {
         const int bb = u / ntile - b_first;
         const int i0 = (u % ntile) * P1_ROWS;
@@ -629,25 +629,31 @@ __global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
 // while the current one is multiplied. int4 units run without prefetch.
 constexpr int P2_MAXB = 16;
 
-constexpr int P2_C = 8;          // 64-wide K chunks per wave (inter <= 512)
-
-// A unit's W2 rows in registers, as in gemm1's P1W (nine 16-byte loads in
-// either layout):
+// C = 64-wide K chunks per wave: 8 (inter <= 512) or 12 (inter <= 768).
+//
+// A unit's W2 rows in registers, as in gemm1's P1W (C + 1 16-byte loads in
+// either layout, no branch between them):
 // * FP8 slot: r[c] = 16 codes of this lane's row, bytes [c 64 + q 16, +16);
-//   r[8] = fp32 row scales of the C rows 4q..4q+3.
+//   r[C] = fp32 row scales of the C rows 4q..4q+3.
 // * int4 slot: r[g] = 32 nibbles of this lane's row, K group g, elements
-//   [g 128 + q 32, +32) (g < 4); r[4] = (scale, zero) of the row for groups
-//   0..3; r[5..8] repeat r[4] (unused).
-struct P2W { i32x4 r[9]; };
-struct P2H { i32x4 v[P2_C][2]; };
+//   [g 128 + q 32, +32) (g < C / 2); r[C / 2 + g / 4] holds the row's
+//   (scale, zero) of group g at dword g % 4; the other registers repeat
+//   that area (unused).
+template <int C>
+struct P2W { i32x4 r[C + 1]; };
+template <int C>
+struct P2H { i32x4 v[C][2]; };
 
-__device__ __forceinline__ void p2_landed(const P2W& W) {
+template <int C>
+__device__ __forceinline__ void p2_landed(const P2W<C>& W) {
 #pragma unroll
-    for (int i = 0; i < 9; ++i) asm volatile("" ::"v"(W.r[i]));
+    for (int i = 0; i <= C; ++i) asm volatile("" ::"v"(W.r[i]));
 }
 
-__device__ __forceinline__ void p2_issue_w(P2W& W, const SlotView& pool, int slot, int fmt, int n0, int m, int q,
+template <int C>
+__device__ __forceinline__ void p2_issue_w(P2W<C>& W, const SlotView& pool, int slot, int fmt, int n0, int m, int q,
                                            int I, int chunks) {
+    constexpr int NSZ = (C / 2 + 3) / 4;                 // 16-byte (scale, zero) loads per row
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
     const int groups = I / MOE_INT4_G;
     const uint8_t* wr8 = sb + pool.off[0][2] + (size_t)(n0 + m) * I + q * 16;
@@ -655,19 +661,20 @@ __device__ __forceinline__ void p2_issue_w(P2W& W, const SlotView& pool, int slo
     const uint8_t* wr4 = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2) + q * 16;
     const uint8_t* sz4 = sb + pool.off[1][3] + (size_t)(n0 + m) * groups * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < C; ++i) {
         const uint8_t* p8 = wr8 + min(i, chunks - 1) * 64;
-        const uint8_t* p4 = i < 4 ? wr4 + min(i, max(groups, 1) - 1) * 64 : sz4;
+        const uint8_t* p4 = i < C / 2 ? wr4 + min(i, max(groups, 1) - 1) * 64 : sz4 + 16 * min(i - C / 2, NSZ - 1);
         W.r[i] = *(const i32x4*)(fmt ? p4 : p8);
     }
-    W.r[8] = *(const i32x4*)(fmt ? sz4 : sc8);
+    W.r[C] = *(const i32x4*)(fmt ? sz4 : sc8);
 }
 
 // h row of this lane's position in the K order of the block's W2 layout
 // (zero for a padding position)
-__device__ __forceinline__ void p2_issue_h(P2H& Hh, const uint16_t* hr, bool valid, int fmt, int q, int chunks) {
+template <int C>
+__device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, bool valid, int fmt, int q, int chunks) {
 #pragma unroll
-    for (int c = 0; c < P2_C; ++c) {
+    for (int c = 0; c < C; ++c) {
         const int k0 = fmt ? (c >> 1) * 128 + q * 32 + (c & 1) * 16 : c * 64 + q * 16;
         if (c < chunks && valid) {
             Hh.v[c][0] = *(const i32x4*)(hr + k0);
@@ -679,6 +686,7 @@ __device__ __forceinline__ void p2_issue_h(P2H& Hh, const uint16_t* hr, bool val
     }
 }
 
+template <int P2_C>
 __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
@@ -707,15 +715,15 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     if (nblk == 0) return;
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
 
-    P2W WA, WB;
-    P2H Hh;
+    P2W<P2_C> WA, WB;
+    P2H<P2_C> Hh;
     int hblock = -1;
     float wt = 0.f;
     {
         const int s0 = s_slot[0];
         if (s0 >= 0) p2_issue_w(WA, pool, s0, fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
     }
-    auto step = [&](int u, P2W& Wc, P2W& Wn) {
+    auto step = [&](int u, P2W<P2_C>& Wc, P2W<P2_C>& Wn) {
         const int bb = u / ntile - b_first;
         const int n0 = (u % ntile) * G2_COLS + wv * 16;
         const int slot = s_slot[bb];
@@ -746,7 +754,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
                 acc = mfma_bf16_16x16x32(a0, h0, acc);
                 acc = mfma_bf16_16x16x32(a1, h1, acc);
             }
-            acc *= __builtin_bit_cast(f32x4, Wc.r[8]);
+            acc *= __builtin_bit_cast(f32x4, Wc.r[P2_C]);
         } else {
             // (q - z) exactly in bf16, each group's scale after its matrix
             // instructions; the scales of C rows 4q..4q+3 from the lanes that
@@ -754,7 +762,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
 #pragma unroll
             for (int g = 0; g < P2_C / 2; ++g) {
                 if (g >= groups) break;                // uniform
-                const uint32_t sz = (uint32_t)Wc.r[4][g];
+                const uint32_t sz = (uint32_t)Wc.r[P2_C / 2 + g / 4][g % 4];
                 const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
                 f32x4 t4 = {0, 0, 0, 0};
 #pragma unroll
@@ -904,9 +912,12 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
     }
     const int units2 = nb * (H / G2_COLS);
     const int per2 = (units2 + pipe_grid - 1) / pipe_grid;
-    if (BM == 16 && I <= 64 * P2_C && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
-        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv, n_slots,
-                   NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+    if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
+        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel<8>, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+    } else if (BM == 16 && I <= 64 * 12 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
+        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel<12>, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
     } else {
         MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(units2), dim3(G_THREADS), 0, stream, sv,
                    n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
