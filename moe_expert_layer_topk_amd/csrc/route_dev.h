@@ -40,8 +40,9 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
 // Lane r < found returns choice r in (id, weight); lanes >= found return
 // (-1, 0). VPL = logits held per lane, entry i of lane l is expert 64 i + l
 // (E <= 64 * VPL). Each round takes the largest logit image; among equal
-// images the lowest expert id (lowest i, then lowest lane) wins. Whole wave
-// must call.
+// images the lowest expert id (lowest i, then lowest lane) wins. Each lane
+// keeps its own largest key and index, so a round is one wave-wide max plus,
+// when a single lane holds it, one lane read. Whole wave must call.
 template <int VPL>
 __device__ __forceinline__ int route_token(const float* __restrict__ row, const uint8_t* __restrict__ mask, int E,
                                            int k, int& my_id, float& my_w) {
@@ -53,23 +54,42 @@ __device__ __forceinline__ int route_token(const float* __restrict__ row, const 
         const bool ok = e < E && (mask == nullptr || mask[e] != 0);
         key[i] = ok ? route_ord(row[e]) : 0u;
     }
+    // this lane's largest key and the lowest index holding it
+    uint32_t lb = 0;
+    int li = 0;
+    auto local_max = [&]() __attribute__((always_inline)) {
+        lb = key[0];
+        li = 0;
+#pragma unroll
+        for (int i = 1; i < VPL; ++i) {
+            const bool gt = key[i] > lb;
+            lb = gt ? key[i] : lb;
+            li = gt ? i : li;
+        }
+    };
+    local_max();
     uint32_t my_ord = 0;
     my_id = -1;
     int found = 0;
     for (int r = 0; r < k; ++r) {
-        uint32_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u32_dpp(best);
+        const uint32_t best = wave_max_u32_dpp(lb);
         if (best == 0) break;                            // uniform across the wave
-        int sel = -1;
+        const uint64_t at = __ballot(lb == best);
+        int sel;
+        if (__popcll(at) == 1) {                         // one lane holds the maximum: its lowest index
+            const int wl = (int)__builtin_ctzll(at);
+            sel = __builtin_amdgcn_readlane(li, wl) * MOE_WAVE + wl;
+        } else {                                         // equal keys in several lanes: lowest expert id
+            sel = -1;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const uint64_t b = __ballot(key[i] == best);
-            if (sel < 0 && b != 0) sel = i * MOE_WAVE + (int)__builtin_ctzll(b);
+            for (int i = 0; i < VPL; ++i) {
+                const uint64_t bi = __ballot(key[i] == best);
+                if (sel < 0 && bi != 0) sel = i * MOE_WAVE + (int)__builtin_ctzll(bi);
+            }
         }
 #pragma unroll
         for (int i = 0; i < VPL; ++i) key[i] = (i * MOE_WAVE + lane == sel) ? 0u : key[i];
+        if (lane == (sel & (MOE_WAVE - 1))) local_max();
         if (lane == r) {
             my_ord = best;
             my_id = sel;
