@@ -212,12 +212,15 @@ MID = Config("mid", 70, (300, 50), 256, 128, 16, 4, 1, 0.1, True, slots=0)
 MIX = Config("mix", 71, (200, 40), 256, 128, 16, 4, 1, 0.1, True, slots=0, int4_frac=0.4, resident_all_at=1)
 # several K steps in both products (H / 128 = 4, I / 128 = 3), ragged blocks, int4 mixed in
 WIDE = Config("wide", 72, (700,), 512, 384, 24, 6, 1, 0.1, True, slots=0, int4_frac=0.25, resident_all_at=1)
+# inter 640: the decode down kernel's 12-chunk variant (FP8 and int4 slots), five int4 groups along K
+LONGI = Config("longi", 73, (40, 200), 256, 640, 16, 4, 1, 0.1, True, slots=0, int4_frac=0.4, resident_all_at=1)
 
 
 @pytest.mark.parametrize("cfg,T,act_mode,block_m", [(MID, 300, 1, 64), (MID, 300, 1, 128), (MID, 50, 0, 16),
                                                     (MID, 50, 0, 64), (MID, 50, 1, 64), (MIX, 200, 1, 128),
                                                     (MIX, 40, 0, 16), (MIX, 40, 0, 32), (MIX, 40, 1, 64),
-                                                    (WIDE, 700, 1, 128), (WIDE, 700, 1, 64)])
+                                                    (WIDE, 700, 1, 128), (WIDE, 700, 1, 64), (LONGI, 40, 0, 16),
+                                                    (LONGI, 200, 1, 128)])
 def test_layer_mid_sizes(gpu, cfg, T, act_mode, block_m):
     run_layer(make_layer(cfg, T, 0), make_bank(cfg), gpu, block_m, act_mode)
 
