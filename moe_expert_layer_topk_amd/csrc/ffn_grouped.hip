@@ -152,30 +152,59 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
     const uint8_t* sz13 = sb + pool.off[1][1];
     for (int g = 0; g < groups; ++g) {
         const int k0 = g * 128;
-        // stage A: BM gathered rows x 128 bytes
-        for (int i = threadIdx.x; i < BM * 8; i += GT) {
-            int r = i >> 3, ch = i & 7;
-            int t = s_tok[r];
-            i32x4 v = {0, 0, 0, 0};
-            if (t >= 0) v = *(const i32x4*)(xq + (size_t)t * H + k0 + ch * 16);
-            *(i32x4*)(sA + r * LDS_ROW + ch * 16) = v;
+        // every load of the step first (one round trip), then the LDS writes.
+        // A: BM gathered rows x 128 bytes; B: 256 weight rows x 128 K (gate
+        // rows c0.., up rows I+c0..); int4: the codes, the zeros of the rows
+        // staged and the scales of this lane's four output columns
+        constexpr int NA = (BM * 8 + GT - 1) / GT, NB = 256 * 8 / GT;
+        i32x4 va[NA];
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int i = threadIdx.x + u * GT;
+            const int t = i < BM * 8 ? s_tok[i >> 3] : -1;
+            va[u] = t >= 0 ? *(const i32x4*)(xq + (size_t)t * H + k0 + (i & 7) * 16) : i32x4{0, 0, 0, 0};
         }
-        // stage B: 256 weight rows x 128 K (gate rows c0.., up rows I+c0..)
-        for (int i = threadIdx.x; i < 256 * 8; i += GT) {
-            int r = i >> 3, ch = i & 7;
-            int col = r & 127;
-            int wrow = (r < 128 ? 0 : I) + c0 + col;
-            i32x4 v = {0, 0, 0, 0};
-            if (col < ncols) {
-                if (fmt == 0) {
-                    v = *(const i32x4*)(w13 + (size_t)wrow * H + k0 + ch * 16);
-                } else {
-                    uint2 pk = *(const uint2*)(w13 + (size_t)wrow * (H / 2) + (k0 + ch * 16) / 2);
-                    float z = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).y;
-                    uint32_t o[4];
-                    int4_to_e4m3_16(pk, z, o);
-                    v = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        i32x4 vb[NB];
+        float zb[NB];
+        float sgu[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int i = threadIdx.x + u * GT;
+            const int r = i >> 3, ch = i & 7, col = r & 127;
+            const int wrow = (r < 128 ? 0 : I) + c0 + (col < ncols ? col : 0);
+            if (fmt == 0) {
+                vb[u] = col < ncols ? *(const i32x4*)(w13 + (size_t)wrow * H + k0 + ch * 16) : i32x4{0, 0, 0, 0};
+            } else {
+                const uint2 pk = col < ncols ? *(const uint2*)(w13 + (size_t)wrow * (H / 2) + (k0 + ch * 16) / 2)
+                                             : make_uint2(0u, 0u);
+                vb[u] = i32x4{(int)pk.x, (int)pk.y, 0, 0};
+                zb[u] = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).y;
+            }
+        }
+        if (fmt == 1) {
+#pragma unroll
+            for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int col = wv * 32 + n * 16 + m;
+                    const int wrow = (gu ? I : 0) + c0 + (col < ncols ? col : 0);
+                    sgu[gu][n] = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).x;
                 }
+        }
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int i = threadIdx.x + u * GT;
+            if (i < BM * 8) *(i32x4*)(sA + (i >> 3) * LDS_ROW + (i & 7) * 16) = va[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int i = threadIdx.x + u * GT;
+            const int r = i >> 3, ch = i & 7, col = r & 127;
+            i32x4 v = vb[u];
+            if (fmt == 1) {
+                uint32_t o[4];
+                int4_to_e4m3_16(make_uint2((uint32_t)vb[u][0], (uint32_t)vb[u][1]), zb[u], o);
+                v = col < ncols ? i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]} : i32x4{0, 0, 0, 0};
             }
             *(i32x4*)(sB + r * LDS_ROW + ch * 16) = v;
         }
@@ -207,10 +236,7 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
 #pragma unroll
                     for (int n = 0; n < 2; ++n) {
                         f32x4 t4 = mfma_fp8_16x16x128(af, bf[gu][n], f32x4{0, 0, 0, 0}, sa, 127);
-                        const int col = wv * 32 + n * 16 + m;
-                        const int wrow = (gu ? I : 0) + c0 + (col < ncols ? col : 0);
-                        const float s = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).x;
-                        acc[a][gu][n] += s * t4;
+                        acc[a][gu][n] += sgu[gu][n] * t4;
                     }
             }
         }
@@ -507,7 +533,7 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
         const int* olist = nullptr;
         const int* n_olist = nullptr;
         mfma_other_list(w.mm, H, cap, &olist, &n_olist);
-        const int oy = cap / BM < 64 ? cap / BM : 64;
+        const int oy = cap / BM < 512 ? cap / BM : 512;     // listed blocks side by side, idle rows exit at once
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 0, stream);
         if (e != hipSuccess) return e;
