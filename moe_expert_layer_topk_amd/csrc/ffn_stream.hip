@@ -796,51 +796,52 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
 template <typename YT, int KMAX>
 __global__ void __launch_bounds__(256) combine_rows_kernel(const YT* __restrict__ ybuf, const float* __restrict__ topk_w,
                                                           int T, int k, int H, uint16_t* __restrict__ out) {
-    const long n8 = (long)T * (H / 8);
-    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (long)gridDim.x * blockDim.x) {
-        const int t = (int)(i / (H / 8)), c = (int)(i % (H / 8)) * 8;
-        float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        // every load first (rows of unfilled route entries are read but not used)
+    // workgroups walk tokens; a token's weights are wave-uniform (scalar
+    // loads), each thread sums 8 columns of the token's k rows
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
         float wj[KMAX];
-        i32x4 v[KMAX][sizeof(YT) == 4 ? 2 : 1];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            wj[j] = 0.f;
-            if (j < k) {
-                wj[j] = topk_w[(size_t)t * k + j];
-                const YT* row = ybuf + ((size_t)t * k + j) * H + c;
-                v[j][0] = *(const i32x4*)row;
-                if constexpr (sizeof(YT) == 4) v[j][1] = *(const i32x4*)(row + 4);
-            }
-        }
+        for (int j = 0; j < KMAX; ++j) wj[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+        for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+            float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            // every load first (rows of unfilled route entries are read but not used)
+            i32x4 v[KMAX][sizeof(YT) == 4 ? 2 : 1];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            const bool use = j < k && wj[j] != 0.f;
-            if constexpr (sizeof(YT) == 4) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    s[d] += use ? __int_as_float(v[j][0][d]) : 0.f;
-                    s[4 + d] += use ? __int_as_float(v[j][1][d]) : 0.f;
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    s[2 * d] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] & 0xFFFF)) : 0.f;
-                    s[2 * d + 1] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] >> 16)) : 0.f;
+            for (int j = 0; j < KMAX; ++j) {
+                if (j < k) {
+                    const YT* row = ybuf + ((size_t)t * k + j) * H + c;
+                    v[j][0] = *(const i32x4*)row;
+                    if constexpr (sizeof(YT) == 4) v[j][1] = *(const i32x4*)(row + 4);
                 }
             }
-        }
-        i32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = (int)two_bf16(s[2 * d], s[2 * d + 1]);
-        *(i32x4*)(out + (size_t)t * H + c) = o;
+            for (int j = 0; j < KMAX; ++j) {
+                const bool use = j < k && wj[j] != 0.f;
+                if constexpr (sizeof(YT) == 4) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        s[d] += use ? __int_as_float(v[j][0][d]) : 0.f;
+                        s[4 + d] += use ? __int_as_float(v[j][1][d]) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        s[2 * d] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] & 0xFFFF)) : 0.f;
+                        s[2 * d + 1] += use ? bf16_to_f32((uint16_t)((uint32_t)v[j][0][d] >> 16)) : 0.f;
+                    }
+                }
+            }
+            i32x4 o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[d] = (int)two_bf16(s[2 * d], s[2 * d + 1]);
+            *(i32x4*)(out + (size_t)t * H + c) = o;
+        }
     }
 }
 
 hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
                               hipStream_t stream) {
-    const long n8 = (long)T * (H / 8);
-    const int blocks = (int)((n8 + 255) / 256 < 2048 ? (n8 + 255) / 256 : 2048);
+    const int blocks = T < 4096 ? T : 4096;
     if (k <= 8)
         MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 8>), dim3(blocks), dim3(256), 0, stream, ybuf, topk_w,
                    T, k, H, out);
@@ -855,8 +856,7 @@ hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int
 
 hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
                                hipStream_t stream) {
-    const long n8 = (long)T * (H / 8);
-    const int blocks = (int)((n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096);
+    const int blocks = T < 4096 ? T : 4096;
     if (k <= 8)
         MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, 8>), dim3(blocks), dim3(256), 0, stream, ybuf,
                    topk_w, T, k, H, out);
