@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--act", choices=["auto", "bf16", "fp8"], default="auto")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--calls", choices=("layer", "split"), default="layer",
+                    help="layer: one moe_layer call per layer; split: moe_route_align then moe_expert_ffn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -108,6 +110,8 @@ def main():
                                    device=dev),
                    fws=torch.empty(max(1, moe.ffn_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
                                    device=dev),
+                   lws=torch.empty(max(1, moe.layer_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
+                                   device=dev),
                    out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
         layers.append((li, pool, x, logits, soe, mask, buf))
     del bdev
@@ -116,6 +120,10 @@ def main():
 
     def run_layer(entry, stream):
         li, pool, x, logits, soe, mask, b = entry
+        if args.calls == "layer":
+            moe.layer_call(pool, x, logits, k, soe, bm, act, mask=mask, ids=b["ids"], w=b["w"], aligned=b["al"],
+                           err=b["err"], out=b["out"], ws=b["lws"], stream=stream)
+            return
         moe.route_align(logits, k, bm, soe, mask=mask, ids=b["ids"], w=b["w"], out=b["al"], err=b["err"],
                         ws=b["aws"] if b["aws"].numel() > 1 else None, stream=stream)
         moe.expert_ffn(pool, x, k, E, b["w"], b["al"], bm, act, out=b["out"], ws=b["fws"], stream=stream)

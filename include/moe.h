@@ -157,6 +157,26 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
                    int block_m, int act_mode, uint16_t* d_out,
                    void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- whole layer
+ * The three steps above in one call: the results of moe_route_align followed
+ * by moe_expert_ffn on the same stream, every output written as those calls
+ * write it (d_err is i32[2] as in moe_route_align; counts are added).
+ * [MG] sections 1 and 3 and [VEP] "hierarchical paging of expert weights"
+ * define the sort; [PW] "what was released" the routing and the mixing.
+ * Decode-sized layers (T <= 64, T*k <= 512, block_m 16, MOE_ACT_BF16,
+ * hidden <= 2048) take fewer launches: every workgroup of the gate/up kernel
+ * sorts the pairs in its own LDS instead of waiting for an align launch, and
+ * for T <= 16 also routes the tokens itself; other shapes run the separate
+ * calls' kernels. The workspace holds moe_layer_workspace_bytes bytes (0 =
+ * invalid arguments). Errors: MOE_EINVAL for the arguments any of the three
+ * calls rejects. */
+size_t moe_layer_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode);
+int moe_layer(const moe_slot_pool* pool, const float* d_logits, const uint8_t* d_mask, const uint16_t* d_x,
+              int T, int E, int k, int block_m, int act_mode, const int32_t* d_slot_of_expert,
+              int32_t* d_topk_ids, float* d_topk_w, int32_t* d_sorted_pair, int32_t* d_block_slot,
+              int32_t* d_counts, int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err,
+              uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- dequant
  * [PW] "technically interesting points": per-expert bit width. Writes the
  * dequantized matrices of slot `slot` in fp32: d_w13 [2I][H], d_w2 [H][I]

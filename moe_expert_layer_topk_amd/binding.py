@@ -48,6 +48,9 @@ def _declare(lib):
         "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
         "moe_expert_ffn": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
                                    c_int, c_int, P, P, c_size_t, P]),
+        "moe_layer_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+        "moe_layer": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, c_int, c_int, c_int, c_int, c_int, P,
+                              P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "moe_dequant_slot": (c_int, [ctypes.POINTER(moe_slot_pool), c_int, P, P, P]),
         "moe_profile_enable": (c_int, [c_int]),
         "moe_profile_kernels": (c_int, []),
@@ -289,11 +292,56 @@ def profile_read():
 
 
 # ---------------------------------------------------------------- whole layer
+def layer_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode):
+    return int(lib().moe_layer_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode))
+
+
+def layer_call(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, ids=None, w=None, aligned=None,
+               err=None, out=None, ws=None, stream=None):
+    """moe_layer: route, align and expert FFN in one call. Returns (out, ids,
+    w, aligned dict); the aligned dict's "err" is i32[2] (route count, align
+    count)."""
+    import torch
+    T, H = x.shape
+    E = logits.shape[1]
+    dev = x.device
+    cap = align_capacity(T, k, E, block_m)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    aligned = _align_out(T, k, E, block_m, dev) if aligned is None else aligned
+    err = torch.zeros(2, dtype=torch.int32, device=dev) if err is None else err
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    need = layer_workspace_bytes(T, k, E, pool.hidden, pool.inter, block_m, act_mode)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().moe_layer(pool.c_ref(), _ptr(logits, torch.float32, T * E, "logits"),
+                           _ptr(mask, torch.uint8, E, "mask"), _ptr(x, torch.bfloat16, T * H, "x"), T, E, k,
+                           block_m, act_mode, _ptr(slot_of_expert, torch.int32, E, "slot_of_expert"),
+                           _ptr(ids, torch.int32, T * k, "ids"), _ptr(w, torch.float32, T * k, "w"),
+                           _ptr(aligned["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                           _ptr(aligned["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                           _ptr(aligned["counts"], torch.int32, E, "counts"),
+                           _ptr(aligned["seg_offset"], torch.int32, E + 1, "seg_offset"),
+                           _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
+                           _ptr(err, torch.int32, 2, "err"), _ptr(out, torch.bfloat16, T * H, "out"),
+                           _ptr(ws, torch.uint8, need, "ws"), c_size_t(ws.numel()), _stream(stream)))
+    aligned = dict(aligned)
+    aligned["err"] = err
+    return out, ids, w, aligned
+
+
 def layer(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, stream=None, fused=False):
     """route -> align -> expert FFN on one stream; returns (out, route, align).
-    fused=True routes and aligns through moe_route_align (then the route
-    error count is aligned["err"][0:1] and align's is aligned["err"][1:2])."""
+    fused=False: moe_route, moe_align, moe_expert_ffn; fused=True: moe_route_align
+    then moe_expert_ffn; fused="layer": moe_layer. With fused set, the route
+    error count is returned as route[2] and align's as aligned["err"]."""
     E = logits.shape[1]
+    if fused == "layer":
+        out, ids, w, al = layer_call(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=mask,
+                                     stream=stream)
+        rerr = al["err"][0:1]
+        al["err"] = al["err"][1:2]
+        return out, (ids, w, rerr), al
     if fused:
         ids, w, al = route_align(logits, k, block_m, slot_of_expert, mask=mask, stream=stream)
         rerr = al["err"][0:1]

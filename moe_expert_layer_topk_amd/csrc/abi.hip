@@ -202,6 +202,47 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
     return MOE_EINVAL;
 }
 
+size_t moe_layer_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode) {
+    const size_t ffn = moe_ffn_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode);
+    if (ffn == 0) return 0;
+    return up256(moe_route_align_workspace_bytes(T, k, E, block_m)) + ffn;
+}
+
+int moe_layer(const moe_slot_pool* pool, const float* d_logits, const uint8_t* d_mask, const uint16_t* d_x, int T,
+              int E, int k, int block_m, int act_mode, const int32_t* d_slot_of_expert, int32_t* d_topk_ids,
+              float* d_topk_w, int32_t* d_sorted_pair, int32_t* d_block_slot, int32_t* d_counts,
+              int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err, uint16_t* d_out, void* d_ws,
+              size_t ws_bytes, void* stream) {
+    moe::PoolArgs pa;
+    if (!pool_args(pool, &pa)) return MOE_EINVAL;
+    if (!d_logits || !d_x || !d_slot_of_expert || !d_topk_ids || !d_topk_w || !d_sorted_pair || !d_block_slot ||
+        !d_counts || !d_seg_offset || !d_n_padded || !d_err || !d_out || !d_ws)
+        return MOE_EINVAL;
+    if (T < 1 || E < 1 || E > MOE_MAX_E || k < 1 || k > E || k > MOE_MAX_K || !valid_block_m(block_m))
+        return MOE_EINVAL;
+    if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
+    const size_t need = moe_layer_workspace_bytes(T, k, E, pa.hidden, pa.inter, block_m, act_mode);
+    if (need == 0 || ws_bytes < need) return MOE_EINVAL;
+    const int cap = capacity(T, k, E, block_m);
+    if (act_mode == MOE_ACT_BF16 && moe::layer_stream_ok(T, k, E, pa.hidden, pa.inter, block_m, cap)) {
+        const size_t aws = up256(moe_route_align_workspace_bytes(T, k, E, block_m));
+        clear_stale_error();
+        return hip_status(moe::launch_layer_stream(pa, d_logits, d_mask, d_slot_of_expert, E, d_x, T, k, d_topk_ids,
+                                                   d_topk_w, d_sorted_pair, d_block_slot, d_counts, d_seg_offset,
+                                                   d_n_padded, d_err, cap, d_out, (uint8_t*)d_ws + aws,
+                                                   (hipStream_t)stream));
+    }
+    // other shapes: the separate calls, on the same stream
+    const size_t aws_bytes = moe_route_align_workspace_bytes(T, k, E, block_m);
+    const size_t aws = up256(aws_bytes);
+    int st = moe_route_align(d_logits, d_mask, T, E, k, block_m, d_slot_of_expert, d_topk_ids, d_topk_w,
+                             d_sorted_pair, d_block_slot, d_counts, d_seg_offset, d_n_padded, d_err,
+                             aws_bytes ? d_ws : nullptr, aws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_expert_ffn(pool, d_x, T, k, E, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded, block_m, act_mode,
+                          d_out, (uint8_t*)d_ws + aws, ws_bytes - aws, stream);
+}
+
 int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream) {
     moe::PoolArgs pa;
     if (!pool_args(pool, &pa)) return MOE_EINVAL;

@@ -24,6 +24,7 @@
 // which leaves the contraction unchanged.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -381,10 +382,231 @@ __device__ __forceinline__ f32x4 p1_int4_mma(const P1W& W, const P1X& X, int q, 
     return acc;
 }
 
+// ------------------------------------------------------------ layer prologue
+// Decode-sized layers (T <= 64 tokens, 16-pair blocks) skip the separate
+// align launch (and, for the smallest batches, the route launch): every
+// workgroup of the gate/up kernel sorts the T*k pairs itself, in LDS, from the
+// route results, so its tables are ready one LDS pass after the ids arrive.
+// The sort is the align call's: MOE-GEN explainer (aibr.jp), sections 1 and
+// 3 (pairs grouped per expert, ascending expert id, ascending pair index
+// inside a segment, each segment padded to the block with the sentinel T*k);
+// vllm-expert-pager article (rand.pepabo.com), "hierarchical paging of expert
+// weights" (block -> slot through the layer's table). A pair's position in its
+// segment is the number of earlier tokens that chose the same expert, read off
+// a per-expert 64-bit token mask (a token lists an expert at most once: the
+// router picks distinct experts). Workgroup 0 writes everything the route and
+// align calls would have written, for the down and combine kernels and the
+// caller; the other workgroups keep only their own blocks' tables.
+constexpr int LAYER_MAX_T = 64;
+constexpr int LAYER_MAX_NP = 512;
+// Route inside the gate/up kernel up to this many tokens (one wavefront per
+// token, every workgroup routes them all); above it the route kernel runs
+// first and the gate/up kernel only sorts the pairs.
+constexpr int LAYER_ROUTE_MAX_T = 16;
+constexpr int LAYER_EPT = MOE_MAX_E / G_THREADS;     // experts per thread
+
+struct LayerIO {
+    const float* logits;            // route inline when not null
+    const uint8_t* mask;
+    const int32_t* slot_of_expert;
+    int E;
+    int32_t* ids;                   // read (route done before) or written by workgroup 0
+    float* w;                       // written by workgroup 0 when routing inline
+    int32_t* sorted_pair;           // outputs of workgroup 0
+    int32_t* block_slot;
+    int32_t* counts;
+    int32_t* seg_offset;
+    int32_t* n_padded;
+    int32_t* err;                   // [0] route, [1] align
+};
+
+struct P1Range { int u_begin, u_end, b_first, nblk; };
+
+template <int RVPL>
+__device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_t* __restrict__ fmt, int n_slots,
+                                                  int T, int k, int ntile, uint8_t* s_fmt, int* s_slot,
+                                                  int (*s_pr)[16]) {
+    __shared__ unsigned long long s_tok[MOE_MAX_E];  // bit t: token t chose the expert
+    __shared__ int s_cnt[MOE_MAX_E];
+    __shared__ int s_off[MOE_MAX_E];
+    __shared__ int s_ids[LAYER_MAX_NP];
+    __shared__ int s_wsum[G_WAVES];
+    constexpr int RT = RVPL == 0 ? 1 : LAYER_ROUTE_MAX_T / G_WAVES;   // tokens per wavefront when routing
+    constexpr int FV = MOE_MAX_SLOTS / G_THREADS;
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid / MOE_WAVE;
+    const int NP = T * k, E = L.E;
+    const bool writer = blockIdx.x == 0;
+    // ---- every global load first (one round trip): slot table, format
+    // tags, and the route ids or this wavefront's tokens' logits
+    int slot_e[LAYER_EPT];
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int e = tid * LAYER_EPT + i;
+        slot_e[i] = e < E ? L.slot_of_expert[e] : -1;
+    }
+    // (ints, not bytes, and no branch around the loads: either made the
+    // compiler wait for each load before issuing the next)
+    int fv[FV];
+#pragma unroll
+    for (int i = 0; i < FV; ++i) fv[i] = fmt[min(tid + i * G_THREADS, n_slots - 1)];
+    int pid[2];
+    float lg[RT][RVPL == 0 ? 1 : RVPL];
+    int mk[RVPL == 0 ? 1 : RVPL];
+    if constexpr (RVPL == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) pid[j] = tid + j * G_THREADS < NP ? L.ids[tid + j * G_THREADS] : -1;
+    } else {
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            const float* row = L.logits + (size_t)min(wv + j * G_WAVES, T - 1) * E;
+#pragma unroll
+            for (int i = 0; i < RVPL; ++i) lg[j][i] = row[min(i * MOE_WAVE + lane, E - 1)];
+        }
+        // no mask: read a byte that exists (the first format tag) and ignore it
+        const uint8_t* mp = L.mask ? L.mask : fmt;
+        const int mlim = L.mask ? E - 1 : 0;
+#pragma unroll
+        for (int i = 0; i < RVPL; ++i) mk[i] = mp[min(i * MOE_WAVE + lane, mlim)];
+    }
+    // ---- LDS set-up
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int e = tid * LAYER_EPT + i;
+        if (e < E) {
+            s_tok[e] = 0ull;
+            s_cnt[e] = 0;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < FV; ++i)
+        if (tid + i * G_THREADS < n_slots) s_fmt[tid + i * G_THREADS] = (uint8_t)fv[i];
+    if constexpr (RVPL != 0) {
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {               // one wavefront per token
+            const int t = wv + j * G_WAVES;
+            if (t >= T) break;                       // uniform over the wave
+            uint32_t key[RVPL];
+#pragma unroll
+            for (int i = 0; i < RVPL; ++i)
+                key[i] = (i * MOE_WAVE + lane < E && (L.mask == nullptr || mk[i] != 0)) ? route_ord(lg[j][i]) : 0u;
+            int id;
+            float wt;
+            const int found = route_select<RVPL>(key, k, id, wt);
+            if (lane < k) {
+                s_ids[t * k + lane] = id;
+                if (writer) {
+                    L.ids[t * k + lane] = id;
+                    L.w[t * k + lane] = wt;
+                }
+            }
+            if (writer && lane == 0 && found < k) atomicAdd(&L.err[0], 1);
+        }
+    }
+    __syncthreads();
+    if constexpr (RVPL != 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) pid[j] = tid + j * G_THREADS < NP ? s_ids[tid + j * G_THREADS] : -1;
+    }
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int p = tid + j * G_THREADS, e = pid[j];
+        if (p >= NP) continue;
+        if (e >= 0 && e < E) {
+            atomicOr(&s_tok[e], 1ull << (p / k));
+            atomicAdd(&s_cnt[e], 1);
+        } else {
+            ++bad;
+        }
+    }
+    __syncthreads();
+    // padded counts of this thread's experts, then their exclusive scan
+    int c[LAYER_EPT], off[LAYER_EPT], sum = 0;
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int e = tid * LAYER_EPT + i;
+        c[i] = e < E ? s_cnt[e] : 0;
+        off[i] = sum;
+        sum += (c[i] + 15) & ~15;
+        if (slot_e[i] < 0) bad += c[i];             // pairs routed to a non-resident expert
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == MOE_WAVE - 1) s_wsum[wv] = incl;
+    __syncthreads();
+    int base = incl - sum, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < G_WAVES; ++w2) {
+        const int ws = s_wsum[w2];
+        base += w2 < wv ? ws : 0;
+        total += ws;
+    }
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int e = tid * LAYER_EPT + i;
+        off[i] += base;
+        if (e < E) s_off[e] = off[i];
+    }
+    if (writer) {
+#pragma unroll
+        for (int i = 0; i < LAYER_EPT; ++i) {
+            const int e = tid * LAYER_EPT + i;
+            if (e >= E) continue;
+            const int pad = (c[i] + 15) & ~15;
+            L.counts[e] = c[i];
+            L.seg_offset[e] = off[i];
+            for (int b = off[i] / 16; b < (off[i] + pad) / 16; ++b) L.block_slot[b] = slot_e[i];
+            for (int q = off[i] + c[i]; q < off[i] + pad; ++q) L.sorted_pair[q] = NP;
+        }
+        if (tid == 0) {
+            L.seg_offset[E] = total;
+            *L.n_padded = total;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) bad += __shfl_xor(bad, o, 64);
+        if (lane == 0 && bad) atomicAdd(&L.err[1], bad);
+    }
+    // this workgroup's unit range and its blocks' tables
+    P1Range R;
+    const int n_units = (total / 16) * ntile;
+    const int per = (n_units + gridDim.x - 1) / gridDim.x;
+    R.u_begin = blockIdx.x * per;
+    R.u_end = min(n_units, R.u_begin + per);
+    R.b_first = R.u_begin / ntile;
+    R.nblk = R.u_begin < R.u_end ? (R.u_end - 1) / ntile - R.b_first + 1 : 0;
+    for (int i = tid; i < R.nblk * 16; i += G_THREADS) s_pr[i / 16][i % 16] = NP;
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int b0 = max(off[i] / 16, R.b_first);
+        const int b1 = min((off[i] + ((c[i] + 15) & ~15)) / 16, R.b_first + R.nblk);
+        for (int b = b0; b < b1; ++b) s_slot[b - R.b_first] = slot_e[i];
+    }
+    __syncthreads();                                   // sentinels before the pairs
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int p = tid + j * G_THREADS, e = pid[j];
+        if (p >= NP || e < 0 || e >= E) continue;
+        const int t = p / k;
+        const int pos = s_off[e] + (int)__popcll(s_tok[e] & ((1ull << t) - 1ull));
+        if (writer) L.sorted_pair[pos] = p;
+        const int bb = pos / 16 - R.b_first;
+        if (bb >= 0 && bb < R.nblk) s_pr[bb][pos % 16] = p;
+    }
+    return R;
+}
+
+// FUSE 0: the block tables come from a separate align launch. FUSE 1: the
+// pairs are sorted here from the route results (layer_prologue). FUSE 2: the
+// tokens are routed here too (route_select<RVPL>).
+template <int FUSE, int RVPL>
 __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
-    SlotView pool, int n_slots, const uint16_t* __restrict__ x, int NP, int k,
+    SlotView pool, int n_slots, const uint16_t* __restrict__ x, int T, int k,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
-    const int32_t* __restrict__ n_padded, int H, int I, uint16_t* __restrict__ hbuf) {
+    const int32_t* __restrict__ n_padded, int H, int I, uint16_t* __restrict__ hbuf, LayerIO L) {
     __shared__ f32x4 s_red[2][G_WAVES][MOE_WAVE];     // unit u uses half u % 2
     __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
     __shared__ int s_slot[P1_MAXB];
@@ -393,46 +615,61 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     const int m = lane & 15, q = lane >> 4;
     const int ntile = I / P1_ROWS;
     const int groups = H / 128;
-    const int n_units = (*n_padded / 16) * ntile;
-    const int per = (n_units + gridDim.x - 1) / gridDim.x;
-    const int u_begin = blockIdx.x * per;
-    const int u_end = min(n_units, u_begin + per);
-    const int b_first = u_begin / ntile;
-    const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
-    if (nblk == 0) return;
+    const int NP = T * k;
     P1W WA, WB;
     P1X X;
     int xblock = -1;
-    // ---- the descriptors of my blocks and the format tags, and the first
-    // unit's weights, in one round trip. Loads complete in issue order, so the
-    // descriptor loads go first; the weights are loaded in the FP8 layout
-    // before the slot's format is known (an int4 slot is at least as large,
-    // so the loads stay inside it) and loaded again if the slot is int4.
-    const int i0f = threadIdx.x;
-    const int bb0 = i0f / 17, r0 = i0f % 17;
-    uint8_t f0 = 0;
-    int d0 = 0;
-    if (i0f < n_slots) f0 = pool.fmt[i0f];
-    if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
-    __builtin_amdgcn_sched_barrier(0);              // keep the descriptor loads ahead of the weights
-    p1_issue_w(WA, pool, max(block_slot[b_first], 0), 0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i0f < n_slots) s_fmt[i0f] = f0;
-    if (i0f < nblk * 17) {
-        if (r0 == 16) s_slot[bb0] = d0;
-        else s_pr[bb0][r0] = d0;
-    }
-    for (int i = i0f + G_THREADS; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
-    for (int i = i0f + G_THREADS; i < nblk * 17; i += G_THREADS) {
-        const int bb = i / 17, r = i % 17;
-        if (r == 16) s_slot[bb] = block_slot[b_first + bb];
-        else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
-    }
-    barrier_lds();                                   // tables written; the weight loads stay in flight
+    int u_begin, u_end, b_first, nblk;
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
-    if (fmt_of(s_slot[0]) == 1) {                    // the first unit is int4: load it in its own layout
-        p1_landed(WA);
-        p1_issue_w(WA, pool, s_slot[0], 1, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+    if constexpr (FUSE == 0) {
+        const int n_units = (*n_padded / 16) * ntile;
+        const int per = (n_units + gridDim.x - 1) / gridDim.x;
+        u_begin = blockIdx.x * per;
+        u_end = min(n_units, u_begin + per);
+        b_first = u_begin / ntile;
+        nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
+        if (nblk == 0) return;
+        // ---- the descriptors of my blocks and the format tags, and the first
+        // unit's weights, in one round trip. Loads complete in issue order, so
+        // the descriptor loads go first; the weights are loaded in the FP8
+        // layout before the slot's format is known (an int4 slot is at least
+        // as large, so the loads stay inside it) and loaded again if the slot
+        // is int4.
+        const int i0f = threadIdx.x;
+        const int bb0 = i0f / 17, r0 = i0f % 17;
+        uint8_t f0 = 0;
+        int d0 = 0;
+        if (i0f < n_slots) f0 = pool.fmt[i0f];
+        if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
+        __builtin_amdgcn_sched_barrier(0);          // keep the descriptor loads ahead of the weights
+        p1_issue_w(WA, pool, max(block_slot[b_first], 0), 0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0f < n_slots) s_fmt[i0f] = f0;
+        if (i0f < nblk * 17) {
+            if (r0 == 16) s_slot[bb0] = d0;
+            else s_pr[bb0][r0] = d0;
+        }
+        for (int i = i0f + G_THREADS; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+        for (int i = i0f + G_THREADS; i < nblk * 17; i += G_THREADS) {
+            const int bb = i / 17, r = i % 17;
+            if (r == 16) s_slot[bb] = block_slot[b_first + bb];
+            else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
+        }
+        barrier_lds();                               // tables written; the weight loads stay in flight
+        if (fmt_of(s_slot[0]) == 1) {                // the first unit is int4: load it in its own layout
+            p1_landed(WA);
+            p1_issue_w(WA, pool, s_slot[0], 1, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        }
+    } else {
+        const P1Range R = layer_prologue<RVPL>(L, pool.fmt, n_slots, T, k, ntile, s_fmt, s_slot, s_pr);
+        u_begin = R.u_begin;
+        u_end = R.u_end;
+        b_first = R.b_first;
+        nblk = R.nblk;
+        if (nblk == 0) return;                       // uniform over the workgroup
+        barrier_lds();
+        p1_issue_w(WA, pool, max(s_slot[0], 0), fmt_of(s_slot[0]), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I,
+                   groups);
     }
     auto step = [&](int u, P1W& Wc, P1W& Wn) {
         const int bb = u / ntile - b_first;
@@ -892,24 +1129,12 @@ size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
 }
 
 template <int BM>
-static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, const float* topk_w,
-                             const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded, int cap,
-                             int H, int I, uint16_t* hbuf, float* ybuf, hipStream_t stream) {
+static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, const float* topk_w,
+                                const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
+                                int cap, int H, int I, const uint16_t* hbuf, float* ybuf, hipStream_t stream) {
     const int NP = T * k;
-    const int nb = cap / BM;                        // blocks that can exist; the kernels skip the rest
-    const int units = nb * (I / ROWS);
+    const int nb = cap / BM;
     const int pipe_grid = 2 * device_cus();
-    // the pipelined kernel: 16-pair blocks, hidden <= 2048, and each workgroup's
-    // unit range must span at most P1_MAXB blocks (always true unless the grid is tiny)
-    const int pipe_units = nb * (I / P1_ROWS);
-    const int per = (pipe_units + pipe_grid - 1) / pipe_grid;
-    if (BM == 16 && H <= 128 * G_WAVES * P1_G && per / (I / P1_ROWS) + 2 <= P1_MAXB) {
-        MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_pipe_kernel, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
-                   n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
-    } else {
-        MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(units), dim3(G_THREADS), 0, stream, sv,
-                   n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
-    }
     const int units2 = nb * (H / G2_COLS);
     const int per2 = (units2 + pipe_grid - 1) / pipe_grid;
     if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
@@ -922,6 +1147,29 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
         MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(units2), dim3(G_THREADS), 0, stream, sv,
                    n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
     }
+}
+
+template <int BM>
+static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, const float* topk_w,
+                             const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded, int cap,
+                             int H, int I, uint16_t* hbuf, float* ybuf, hipStream_t stream) {
+    const int NP = T * k;
+    const int nb = cap / BM;                        // blocks that can exist; the kernels skip the rest
+    const int units = nb * (I / ROWS);
+    const int pipe_grid = 2 * device_cus();
+    // the pipelined kernel: 16-pair blocks, hidden <= 2048, and each workgroup's
+    // unit range must span at most P1_MAXB blocks (always true unless the grid is tiny)
+    const int pipe_units = nb * (I / P1_ROWS);
+    const int per = (pipe_units + pipe_grid - 1) / pipe_grid;
+    if (BM == 16 && H <= 128 * G_WAVES * P1_G && per / (I / P1_ROWS) + 2 <= P1_MAXB) {
+        MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<0, 0>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
+                   sv, n_slots, x, T, k, sorted_pair, block_slot, n_padded, H, I, hbuf, LayerIO{});
+    } else {
+        MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(units), dim3(G_THREADS), 0, stream, sv,
+                   n_slots, x, NP, k, sorted_pair, block_slot, n_padded, H, I, hbuf);
+    }
+    launch_gemm2_stream<BM>(sv, n_slots, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf,
+                            stream);
 }
 
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
@@ -945,6 +1193,59 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_combine_f32(ybuf, topk_w, T, k, H, out, stream);
+}
+
+// ------------------------------------------------------------ whole layer
+bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
+    if (block_m != 16 || T > LAYER_MAX_T || T * k > LAYER_MAX_NP || E > MOE_MAX_E) return false;
+    if (H > 128 * G_WAVES * P1_G) return false;
+    const int pipe_grid = 2 * device_cus();
+    const int per = ((cap / 16) * (I / P1_ROWS) + pipe_grid - 1) / pipe_grid;
+    return per / (I / P1_ROWS) + 2 <= P1_MAXB;
+}
+
+template <int RVPL>
+static void launch_gemm1_layer(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, int H, int I,
+                               uint16_t* hbuf, const LayerIO& L, hipStream_t stream) {
+    MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<RVPL == 0 ? 1 : 2, RVPL>), dim3(2 * device_cus()),
+               dim3(G_THREADS), 0, stream, sv, n_slots, x, T, k, (const int32_t*)nullptr, (const int32_t*)nullptr,
+               (const int32_t*)nullptr, H, I, hbuf, L);
+}
+
+hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const uint8_t* mask,
+                               const int32_t* slot_of_expert, int E, const uint16_t* x, int T, int k, int32_t* ids,
+                               float* w, int32_t* sorted_pair, int32_t* block_slot, int32_t* counts,
+                               int32_t* seg_offset, int32_t* n_padded, int32_t* err, int cap, uint16_t* out,
+                               void* ws, hipStream_t stream) {
+    SlotView sv;
+    sv.base = (const uint8_t*)pa.base;
+    sv.stride = pa.stride;
+    sv.fmt = pa.fmt;
+    for (int f = 0; f < 2; ++f)
+        for (int p = 0; p < 4; ++p) sv.off[f][p] = pa.off[f][p];
+    const int H = pa.hidden, I = pa.inter;
+    uint16_t* hbuf = (uint16_t*)ws;
+    float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
+    LayerIO L{logits, mask, slot_of_expert, E, ids, w, sorted_pair, block_slot, counts, seg_offset, n_padded, err};
+    if (T <= LAYER_ROUTE_MAX_T) {
+        if (E <= 64) launch_gemm1_layer<1>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        else if (E <= 128) launch_gemm1_layer<2>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        else if (E <= 256) launch_gemm1_layer<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        else if (E <= 512) launch_gemm1_layer<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        else launch_gemm1_layer<16>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+    } else {
+        hipError_t e = launch_route(logits, mask, T, E, k, ids, w, err, stream);
+        if (e != hipSuccess) return e;
+        L.logits = nullptr;
+        launch_gemm1_layer<0>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_gemm2_stream<16>(sv, pa.n_slots, T, k, w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf,
+                            stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_combine_f32(ybuf, w, T, k, H, out, stream);
 }
 
 }  // namespace moe

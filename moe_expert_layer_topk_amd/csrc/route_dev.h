@@ -1,5 +1,5 @@
 // Top-k selection of one token by one wavefront (shared by the route kernel
-// and the fused small-batch route + align kernel).
+// and the gate/up kernel that routes small batches itself).
 //
 // PagedWeight commentary (spectral-agent.com), "what was released" and
 // "technically interesting points": the router sends each token to a few
@@ -37,23 +37,35 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Lane r < found returns choice r in (id, weight); lanes >= found return
-// (-1, 0). VPL = logits held per lane, entry i of lane l is expert 64 i + l
-// (E <= 64 * VPL). Each round takes the largest logit image; among equal
-// images the lowest expert id (lowest i, then lowest lane) wins. Each lane
-// keeps its own largest key and index, so a round is one wave-wide max plus,
-// when a single lane holds it, one lane read. Whole wave must call.
+// Keys of one token's logits, entry i of lane l = expert 64 i + l (E <= 64 *
+// VPL); 0 for experts past E or masked out. Every load is issued before any
+// is used (clamped indices, no branches), so they share one round trip.
 template <int VPL>
-__device__ __forceinline__ int route_token(const float* __restrict__ row, const uint8_t* __restrict__ mask, int E,
-                                           int k, int& my_id, float& my_w) {
+__device__ __forceinline__ void route_keys(const float* __restrict__ row, const uint8_t* __restrict__ mask, int E,
+                                           uint32_t (&key)[VPL]) {
     const int lane = lane_id();
-    uint32_t key[VPL];
+    float v[VPL];
+    int mk[VPL];
+    const uint8_t* mp = mask ? mask : (const uint8_t*)row;   // no mask: read a byte that exists, ignore it
+    const int mlim = mask ? E - 1 : 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int e = i * MOE_WAVE + lane;
-        const bool ok = e < E && (mask == nullptr || mask[e] != 0);
-        key[i] = ok ? route_ord(row[e]) : 0u;
+        v[i] = row[min(i * MOE_WAVE + lane, E - 1)];
+        mk[i] = mp[min(i * MOE_WAVE + lane, mlim)];
     }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        key[i] = (i * MOE_WAVE + lane < E && (mask == nullptr || mk[i] != 0)) ? route_ord(v[i]) : 0u;
+}
+
+// Lane r < found returns choice r in (id, weight); lanes >= found return
+// (-1, 0). Each round takes the largest logit image; among equal images the
+// lowest expert id (lowest i, then lowest lane) wins. Each lane keeps its own
+// largest key and index, so a round is one wave-wide max plus, when a single
+// lane holds it, one lane read. Whole wave must call; key is consumed.
+template <int VPL>
+__device__ __forceinline__ int route_select(uint32_t (&key)[VPL], int k, int& my_id, float& my_w) {
+    const int lane = lane_id();
     // this lane's largest key and the lowest index holding it
     uint32_t lb = 0;
     int li = 0;
@@ -89,7 +101,7 @@ __device__ __forceinline__ int route_token(const float* __restrict__ row, const 
         }
 #pragma unroll
         for (int i = 0; i < VPL; ++i) key[i] = (i * MOE_WAVE + lane == sel) ? 0u : key[i];
-        if (lane == (sel & (MOE_WAVE - 1))) local_max();
+        local_max();                                     // changes only the winner lane's (lb, li)
         if (lane == r) {
             my_ord = best;
             my_id = sel;
@@ -104,6 +116,15 @@ __device__ __forceinline__ int route_token(const float* __restrict__ row, const 
     my_w = (lane < found) ? z / s : 0.f;
     if (lane >= found) my_id = -1;
     return found;
+}
+
+// One token: route_keys then route_select.
+template <int VPL>
+__device__ __forceinline__ int route_token(const float* __restrict__ row, const uint8_t* __restrict__ mask, int E,
+                                           int k, int& my_id, float& my_w) {
+    uint32_t key[VPL];
+    route_keys<VPL>(row, mask, E, key);
+    return route_select<VPL>(key, k, my_id, my_w);
 }
 
 }  // namespace moe

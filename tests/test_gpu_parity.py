@@ -273,6 +273,82 @@ def test_layer_c4_mixed_decode(gpu):
     run_layer(li, make_bank(c), gpu, 64, 1)
 
 
+# ---------------------------------------------------------------- whole layer in one call (moe_layer)
+# E = 1024 experts: the widest router the kernels take (16 logits per lane)
+WIDEE = Config("widee", 74, (12, 40), 128, 64, 1024, 8, 1, 0.1, True, slots=0)
+
+
+def run_layer_call(li, bank, dev, block_m=16, act_mode=0):
+    """moe_layer against the oracle, and bit-identical to the separate calls
+    (route, align, expert FFN) on the same inputs."""
+    import torch
+    out, ref = run_layer(li, bank, dev, block_m, act_mode, fused="layer")
+    out2, _, _ = moe.layer(device_pool(li, bank, dev), *_layer_args(li, dev), block_m, act_mode,
+                           mask=device_inputs(li, dev)[3])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "moe_layer differs from the separate calls"
+    return out, ref
+
+
+def _layer_args(li, dev):
+    x, logits, soe, _ = device_inputs(li, dev)
+    return x, logits, li.cfg.k, soe
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 17, 32, 64])
+def test_layer_call_c1(gpu, T):
+    """Route inside the gate/up kernel up to 16 tokens, the route kernel
+    above; the pairs sorted in every workgroup; T = 64 is the largest
+    decode batch (512 pairs)."""
+    c = CONFIGS["C1"]
+    run_layer_call(make_layer(c, T, 4), make_bank(c), gpu)
+
+
+@pytest.mark.parametrize("T", [16, 32])
+def test_layer_call_c3_masked(gpu, T):
+    c = CONFIGS["C3"]
+    run_layer_call(make_layer(c, T, 2), make_bank(c), gpu)
+
+
+def test_layer_call_c4_mixed(gpu):
+    c = CONFIGS["C4"]
+    li = make_layer(c, 8, 3)
+    assert (li.slot_fmt == 1).any()
+    run_layer_call(li, make_bank(c), gpu)
+
+
+@pytest.mark.parametrize("cfg,T", [(WIDEE, 12), (WIDEE, 40), (LONGI, 40), (MIX, 40), (CONFIGS["C0"], 16)])
+def test_layer_call_shapes(gpu, cfg, T):
+    run_layer_call(make_layer(cfg, T, 0), make_bank(cfg), gpu)
+
+
+def test_layer_call_shortfall(gpu):
+    """One allowed expert for k = 2: every token is short by one; the -1
+    entries are counted by route and align and left out of the FFN."""
+    c = CONFIGS["C0"]
+    li = make_layer(c, 16, 0)
+    li.mask = np.zeros(c.E, np.uint8)
+    li.mask[5] = 1
+    out, ref = run_layer_call(li, make_bank(c), gpu)
+    assert ref["err"] == 16
+
+
+def test_layer_call_nonresident(gpu):
+    """A routed expert without a slot contributes nothing and is counted."""
+    c = CONFIGS["C1"]
+    li = make_layer(c, 8, 1)
+    ids, _, _ = oracle.route(li.logits, li.mask, c.k)
+    for e in (int(ids[0, 0]), int(ids[3, 4])):
+        li.slot_of_expert[e] = -1
+    out, ref = run_layer_call(li, make_bank(c), gpu)
+    assert ref["err"] > 0
+
+
+def test_layer_call_batched_falls_back(gpu):
+    """Shapes outside the decode path run the separate calls' kernels."""
+    run_layer_call(make_layer(MID, 300, 0), make_bank(MID), gpu, 64, 1)
+
+
 @pytest.mark.parametrize("name,T,block_m", [("C2", 16384, 128), ("C4", 8192, 128), ("C3", 4096, 128)])
 def test_layer_batched_full_size_sampled(gpu, name, T, block_m):
     c = CONFIGS[name]
