@@ -37,9 +37,12 @@
 //   row across four fragments are adjacent output columns: epilogue stores
 //   are 4-byte fp8 or 8-byte bf16 runs straight from registers;
 // * per-tile metadata (row scales of the expert, pair ids, route weights)
-//   reaches LDS by direct-to-LDS loads issued with the tile's first stage,
-//   and token ids are read with scalar loads, so no vector load ever waits
-//   behind the stages in flight.
+//   reaches LDS by direct-to-LDS loads issued with the tile's first stage;
+//   the gate/up kernel's token ids of a tile arrive the same way with the
+//   previous tile's first stage, and its workgroup's tile descriptors are
+//   read into LDS once at the start, so setting up a tile and its epilogue
+//   wait for no memory round trip (the down kernel reads descriptors with
+//   scalar loads).
 // A prep kernel lists the FP8 blocks and lays out the per-position token
 // ids, route weights and activation scales the two kernels read. Blocks whose
 // slot is int4-g128 or not resident are handled by the simpler kernels of
@@ -59,7 +62,10 @@ constexpr int MM_STAGE = MM_OPS + 256;
 constexpr int MM_META = 4096;                           // per-tile metadata slot
 constexpr int MM_NMETA = 4;                             // tiles that can be in flight at once
 constexpr int MM_AMAX = MM_RING * MM_STAGE + MM_NMETA * MM_META;
-constexpr int MM_SMEM = MM_AMAX + 2 * MM_TM * 4;
+constexpr int MM_DESC = MM_AMAX + 2 * MM_TM * 4;     // this workgroup's tile descriptors
+constexpr int MM_MAXDESC = 512;                         // held in LDS (later tiles: scalar loads)
+constexpr int MM_SMEM = MM_DESC + 16 * MM_MAXDESC;
+constexpr int MM_TOK = 1024;                            // KIND 0: token ids of the tile, in its metadata slot
 
 template <int V>
 struct IC {
@@ -118,16 +124,10 @@ __device__ __forceinline__ void dma4(const void* src, uint8_t* lds) {
 // Scalar loads for per-tile metadata. A vector load here would be waited for
 // with the direct-to-LDS loads in flight (vector memory completes in order),
 // draining the pipeline; scalar loads count on a separate counter.
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int4 sload4(const int4* p) {
     i32x4 r;
     asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
     return make_int4(r[0], r[1], r[2], r[3]);
-}
-__device__ __forceinline__ i32x16 sload16(const int32_t* p) {
-    i32x16 r;
-    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
-    return r;
 }
 
 // 32 codes of stage row r for the lane group q (K bytes [32 q, 32 q + 32)):
@@ -261,6 +261,34 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     if (nj == 0) return;
     const int N = nj * S;
 
+    // gate/up kernel: this workgroup's tile descriptors into LDS (one round
+    // trip for all) and the token ids of tile 0 into its metadata slot; later
+    // tiles' token ids arrive with the previous tile's first stage
+    // (the down kernel keeps scalar loads: the table measured slower there)
+    int4* s_desc = (int4*)(smem + MM_DESC);
+    if (KIND == 0) {
+        for (int i = threadIdx.x; i < min(nj, MM_MAXDESC); i += MM_THREADS)
+            s_desc[i] = tl.tiles[(start + idx + per_x * i) / NT];
+        __syncthreads();
+    }
+    auto desc_of = [&](int j) __attribute__((always_inline)) {
+        if (KIND == 0 && j < MM_MAXDESC) {
+            const int4 v = s_desc[j];
+            return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                             __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+        }
+        return sload4(tl.tiles + __builtin_amdgcn_readfirstlane((start + idx + per_x * j) / NT));
+    };
+    if (KIND == 0) {
+        const int4 d0 = desc_of(0);
+        int32_t* s_tok = (int32_t*)(smem + MM_RING * MM_STAGE + MM_TOK);
+        if (threadIdx.x < MM_TM) {
+            const int r = threadIdx.x;
+            s_tok[r] = tl.tokrow[(d0.x + (r >= MM_BM && d0.z == 2 ? 1 : 0)) * MM_BM + r % MM_BM];
+        }
+        __syncthreads();
+    }
+
     // metadata dword loads (256 B each) of this wave per tile, into the tile's
     // metadata slot at byte meta_off. KIND 0: wave 1 gate, wave 2 up row scales
     // of the 128 columns; KIND 1: waves 1, 2 pair ids of the two blocks, waves
@@ -277,6 +305,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     const uint8_t* bB = nullptr;          // B rows of this tile
     const uint8_t* bS = nullptr;          // row-scale bytes of this tile (wave 0)
     const uint8_t* bM = nullptr;          // metadata source (meta_n > 0)
+    const int32_t* bT = tl.tokrow;        // KIND 0, waves 4..7: next tile's token ids
     uint32_t oA[4], oB0 = 0, oB1 = 0, oS = 0, oM = 0;   // B row of j: oB(j & 1) + (32 (j & 1) + (j >> 1)) rows
     // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
     // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
@@ -291,7 +320,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         const int brow0 = (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 : (wv >> 2) * 128 + ((wv & 3) >> 1) * 64) +
                           2 * (wv & 1) + 4 * (lane >> 3);
         const int L = start + idx + per_x * j;
-        const int4 d = sload4(tl.tiles + L / NT);
+        const int4 d = desc_of(j);
         const int b = d.x, nt = L % NT, two = d.z == 2;
         const uint8_t* sb = pool.base + (size_t)d.y * pool.stride;
         const int blk_w = b + ((wv >> 2) & two);            // block of this wave's A rows
@@ -299,19 +328,15 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         bS = tl.scl + (size_t)b * S * MM_BM;
         oS = ((lane >> 5) & two) * S * MM_BM + 4 * (lane & 31);
         if (KIND == 0) {
-            const int32_t* tr = tl.tokrow + blk_w * MM_BM + r_w;   // 32 tokens, scalar loads
-            const i32x16 t0 = sload16(tr), t1 = sload16(tr + 16);
-            const int r8 = lane >> 3;
-            int t[4] = {0, 0, 0, 0};
+            // token ids of this wave's 32 rows, from the tile's metadata slot
+            const int32_t* s_tok = (const int32_t*)(smem + MM_RING * MM_STAGE + (j % MM_NMETA) * MM_META + MM_TOK) +
+                                   ((wv >> 2) & 1) * MM_BM + r_w + (lane >> 3);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                t[0] = r8 == r ? t0[r] : t[0];
-                t[1] = r8 == r ? t0[8 + r] : t[1];
-                t[2] = r8 == r ? t1[r] : t[2];
-                t[3] = r8 == r ? t1[8 + r] : t[3];
-            }
-#pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)t[j2] * H + ((j2 & 1) ? csw1 : csw0);
+            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)s_tok[8 * j2] * H + ((j2 & 1) ? csw1 : csw0);
+            // waves 4..7: source of 64 token ids of the next tile (loaded with this tile's first stage)
+            const int4 dn = desc_of(min(j + 1, nj - 1));
+            const int i4 = (wv - 4) & 3;
+            bT = tl.tokrow + (dn.x + (i4 >= 2 && dn.z == 2 ? 1 : 0)) * MM_BM + 64 * (i4 & 1);
             const int c0 = nt * 128;
             bB = sb + pool.off[0] + (size_t)c0 * H;
             oB0 = (uint32_t)brow0 * H + csw0;
@@ -335,7 +360,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     };
     // vector memory operations stage s puts in flight for this wave
     auto stage_ops = [&](int s) __attribute__((always_inline)) {
-        return 8 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n : 0);
+        return 8 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n + (KIND == 0 && wv >= 4 ? 1 : 0) : 0);
     };
     // the loads of step s into LDS buffer u (u = s % 2, except past the end of
     // the stream, where the last step is loaded again into the buffer the
@@ -362,6 +387,9 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         if (g == 0) {
             uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
             for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + om, md + 256 * h);
+            if (KIND == 0 && wv >= 4)
+                dma4((const uint8_t*)bT + om, smem + MM_RING * MM_STAGE + ((s / S + 1) % MM_NMETA) * MM_META + MM_TOK +
+                                                  256 * (wv - 4));
         }
     };
     auto issue = [&](int s, int u) __attribute__((always_inline)) {
@@ -416,7 +444,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     };
     auto epilogue = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
-        const int4 d = sload4(tl.tiles + L / NT);
+        const int4 d = desc_of(j);
         const int b = d.x, nt = L % NT, rows = d.z * MM_BM;
         // opaque copies: row addresses are formed here, not hoisted out of the
         // step loop into registers the loop would then have to spill
