@@ -246,7 +246,11 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
     const int m = lane & 15, q = lane >> 4;
-    const int mw = wv & 3, nw = wv >> 2;                  // 64-row group, 128-column half
+    // 64-row group and 128-column half. Waves w and w + 4 share a SIMD, so
+    // every SIMD holds one wave of each 128-row half of the tile: when a tile
+    // has one block, the waves of its empty half skip their work and every
+    // SIMD does half the matrix work.
+    const int mw = 2 * (wv >> 2) + ((wv >> 1) & 1), nw = wv & 1;
     const int S = KIND == 0 ? H / 128 : I / 128;          // K steps per tile
     const int NT = KIND == 0 ? I / 128 : H / 256;         // column tiles per block pair
     const int hgroups = I / 128;
@@ -306,6 +310,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     const uint8_t* bS = nullptr;          // row-scale bytes of this tile (wave 0)
     const uint8_t* bM = nullptr;          // metadata source (meta_n > 0)
     const int32_t* bT = tl.tokrow;        // KIND 0, waves 4..7: next tile's token ids
+    int two_next = 1;                     // the last tile set up has two blocks
     uint32_t oA[4], oB0 = 0, oB1 = 0, oS = 0, oM = 0;   // B row of j: oB(j & 1) + (32 (j & 1) + (j >> 1)) rows
     // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
     // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
@@ -322,6 +327,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         const int L = start + idx + per_x * j;
         const int4 d = desc_of(j);
         const int b = d.x, nt = L % NT, two = d.z == 2;
+        two_next = two;
         const uint8_t* sb = pool.base + (size_t)d.y * pool.stride;
         const int blk_w = b + ((wv >> 2) & two);            // block of this wave's A rows
         const int r_w = 32 * (wv & 3);                      // first of them inside the block
@@ -428,14 +434,17 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     // between them: a load instruction waits while the CU's load path is
     // busy, and the matrix pipe keeps working on the instructions issued
     // before it
-    auto multiply_issue = [&](int s, int u) __attribute__((always_inline)) {
+    auto multiply_issue = [&](int s, int u, bool live) __attribute__((always_inline)) {
         dma_tail(s, u);                                 // branches: kept out of the sequence below
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
-                acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+                // (a wave of an empty tile half issues the loads only; one
+                // sequence with the test at each instruction keeps the
+                // register allocation of a single path)
+                if (live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
                 const int k = 8 * a + n;
                 if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
                 if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
@@ -528,15 +537,19 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     zero_acc();
     issue(0, 0);
     issue(min(1, N - 1), 1);
+    bool live = true;
     for (int cs = 0; cs < N; ++cs) {
+        // with two or more steps per tile, tile cs / S was the last one set
+        // up when its first step begins
+        if (cs % S == 0 && S >= 2) live = mw < 2 || two_next;
         wait_vm_n(stage_ops(min(cs + 1, N - 1)));       // step cs landed
         barrier_lds();                                  // ... for every wave
-        read_step(smem + (cs % MM_RING) * MM_STAGE);
+        read_step(smem + (cs % MM_RING) * MM_STAGE);   // (a conditional read costs registers)
         barrier_lds();                                  // every wave has read step cs
         __builtin_amdgcn_sched_barrier(0);
         const int s2 = min(cs + 2, N - 1);
         if (cs + 2 < N && s2 % S == 0) setup(s2 / S);
-        multiply_issue(s2, cs % MM_RING);
+        multiply_issue(s2, cs % MM_RING, live);
         if (cs % S == S - 1) {
             epilogue(cs / S);
             zero_acc();
