@@ -33,9 +33,11 @@
 // * 8 waves in a 4 x 2 grid over a 256 x 256 tile, 64 x 128 outputs each:
 //   32 v_mfma_scale_f32_16x16x128_f8f6f4 per wave and K step, with the
 //   power-of-two activation exponents (E8M0) as the instruction's A scales;
-// * B rows are ordered so that the four accumulators a lane holds for one
-//   row across four fragments are adjacent output columns: epilogue stores
-//   are 4-byte fp8 or 8-byte bf16 runs straight from registers;
+// * B rows are ordered so that the accumulators a lane holds for one row
+//   across fragments are adjacent output columns: epilogue stores are 4-byte
+//   fp8 runs (gate/up: four h columns from four gate and four up fragments)
+//   or 16-byte bf16 runs (down: eight columns from eight fragments) straight
+//   from registers;
 // * per-tile metadata (row scales of the expert, pair ids, route weights)
 //   reaches LDS by direct-to-LDS loads issued with the tile's first stage;
 //   the gate/up kernel's token ids of a tile arrive the same way with the
@@ -313,8 +315,9 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     int two_next = 1;                     // the last tile set up has two blocks
     uint32_t oA[4], oB0 = 0, oB1 = 0, oS = 0, oM = 0;   // B row of j: oB(j & 1) + (32 (j & 1) + (j >> 1)) rows
     // B stage row 32 w + 8 j + i / 8 = fragment 2 w + j / 2, fragment row 8 (j & 1) + i / 8;
-    // fragment f = 8 nw + n holds output columns nw * CW + (n / 4) * 64 + 4 m + n % 4
-    // (KIND 0: n / 4 picks gate or up rows, CW = 64; KIND 1: CW = 128)
+    // fragment f = 8 nw + n, row m holds output column
+    //   KIND 0: nw * 64 + (n / 4) * I + 4 m + n % 4 (n / 4 picks gate or up rows)
+    //   KIND 1: nw * 128 + 8 m + n
     auto setup = [&](int j) __attribute__((always_inline)) {
         // per-lane constants formed here from an opaque copy of the lane id,
         // not held in registers across the step loop
@@ -322,8 +325,8 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         asm volatile("" : "+v"(lane));
         const int csw0 = 16 * ((lane & 7) ^ ((lane >> 4) & 1));        // loads j even
         const int csw1 = 16 * ((lane & 7) ^ (4 | ((lane >> 4) & 1)));  // loads j odd
-        const int brow0 = (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 : (wv >> 2) * 128 + ((wv & 3) >> 1) * 64) +
-                          2 * (wv & 1) + 4 * (lane >> 3);
+        const int brow0 = KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 + 2 * (wv & 1) + 4 * (lane >> 3)
+                                    : (wv >> 2) * 128 + 2 * (wv & 3) + 8 * (lane >> 3);
         const int L = start + idx + per_x * j;
         const int4 d = desc_of(j);
         const int b = d.x, nt = L % NT, two = d.z == 2;
@@ -380,7 +383,8 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         uint8_t* st = smem + u * MM_STAGE;
         const int k0 = (s % S) * 128;
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
-        dma16(bB + (32 * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0), st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
+        dma16(bB + ((KIND == 0 ? 32 : 64) * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0),
+              st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
     };
     auto dma_tail = [&](int s, int u) __attribute__((always_inline)) {
         uint8_t* st = smem + u * MM_STAGE;
@@ -501,9 +505,9 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         } else {
             const int32_t* s_pr = (const int32_t*)md;
             const float* s_w = (const float*)(md + 1024);
-            const f32x4 sc0 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 4 * m));
-            const f32x4 sc1 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 64 + 4 * m));
-            const int c = nt * 256 + nw * 128 + 4 * m;
+            const f32x4 sc0 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 8 * m));
+            const f32x4 sc1 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 8 * m + 4));
+            const int c = nt * 256 + nw * 128 + 8 * m;        // 8 adjacent columns: one 16-byte store
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -520,11 +524,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                         v[2 * h] = bf16x2_rne(y0, y1);
                         v[2 * h + 1] = bf16x2_rne(y2, y3);
                     }
-                    if (row < rows && p < NP) {
-                        uint16_t* yr = ybuf + (size_t)p * H + c;
-                        *(uint2*)yr = make_uint2(v[0], v[1]);
-                        *(uint2*)(yr + 64) = make_uint2(v[2], v[3]);
-                    }
+                    if (row < rows && p < NP) *(uint4*)(ybuf + (size_t)p * H + c) = make_uint4(v[0], v[1], v[2], v[3]);
                 }
         }
     };
