@@ -399,9 +399,9 @@ __device__ __forceinline__ f32x4 p1_int4_mma(const P1W& W, const P1X& X, int q, 
 // caller; the other workgroups keep only their own blocks' tables.
 constexpr int LAYER_MAX_T = 64;
 constexpr int LAYER_MAX_NP = 512;
-// Route inside the gate/up kernel up to this many tokens (one wavefront per
-// token, every workgroup routes them all); above it the route kernel runs
-// first and the gate/up kernel only sorts the pairs.
+// Route inside the gate/up kernel up to this many tokens and 512 experts (one
+// wavefront per token, every workgroup routes them all); otherwise the route
+// kernel runs first and the gate/up kernel only sorts the pairs.
 constexpr int LAYER_ROUTE_MAX_T = 16;
 constexpr int LAYER_EPT = MOE_MAX_E / G_THREADS;     // experts per thread
 
@@ -422,7 +422,7 @@ struct LayerIO {
 
 struct P1Range { int u_begin, u_end, b_first, nblk; };
 
-template <int RVPL>
+template <int RVPL, int RT>
 __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_t* __restrict__ fmt, int n_slots,
                                                   int T, int k, int ntile, uint8_t* s_fmt, int* s_slot,
                                                   int (*s_pr)[16]) {
@@ -431,24 +431,22 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
     __shared__ int s_off[MOE_MAX_E];
     __shared__ int s_ids[LAYER_MAX_NP];
     __shared__ int s_wsum[G_WAVES];
-    constexpr int RT = RVPL == 0 ? 1 : LAYER_ROUTE_MAX_T / G_WAVES;   // tokens per wavefront when routing
-    constexpr int FV = MOE_MAX_SLOTS / G_THREADS;
     const int tid = threadIdx.x, lane = lane_id(), wv = tid / MOE_WAVE;
     const int NP = T * k, E = L.E;
     const bool writer = blockIdx.x == 0;
     // ---- every global load first (one round trip): slot table, format
-    // tags, and the route ids or this wavefront's tokens' logits
+    // tags, and the route ids or the logits of this wavefront's RT tokens.
+    // Each load instruction holds its wave for a while as it issues, so only
+    // the loads the shape needs are issued.
     int slot_e[LAYER_EPT];
 #pragma unroll
     for (int i = 0; i < LAYER_EPT; ++i) {
         const int e = tid * LAYER_EPT + i;
         slot_e[i] = e < E ? L.slot_of_expert[e] : -1;
     }
-    // (ints, not bytes, and no branch around the loads: either made the
-    // compiler wait for each load before issuing the next)
-    int fv[FV];
-#pragma unroll
-    for (int i = 0; i < FV; ++i) fv[i] = fmt[min(tid + i * G_THREADS, n_slots - 1)];
+    // (an int, not a byte: bytes packed into one register made the compiler
+    // wait for each load before issuing the next)
+    const int fv0 = fmt[min(tid, n_slots - 1)];
     int pid[2];
     float lg[RT][RVPL == 0 ? 1 : RVPL];
     int mk[RVPL == 0 ? 1 : RVPL];
@@ -462,11 +460,12 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
 #pragma unroll
             for (int i = 0; i < RVPL; ++i) lg[j][i] = row[min(i * MOE_WAVE + lane, E - 1)];
         }
-        // no mask: read a byte that exists (the first format tag) and ignore it
-        const uint8_t* mp = L.mask ? L.mask : fmt;
-        const int mlim = L.mask ? E - 1 : 0;
 #pragma unroll
-        for (int i = 0; i < RVPL; ++i) mk[i] = mp[min(i * MOE_WAVE + lane, mlim)];
+        for (int i = 0; i < RVPL; ++i) mk[i] = 1;
+        if (L.mask) {
+#pragma unroll
+            for (int i = 0; i < RVPL; ++i) mk[i] = L.mask[min(i * MOE_WAVE + lane, E - 1)];
+        }
     }
     // ---- LDS set-up
 #pragma unroll
@@ -477,9 +476,8 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
             s_cnt[e] = 0;
         }
     }
-#pragma unroll
-    for (int i = 0; i < FV; ++i)
-        if (tid + i * G_THREADS < n_slots) s_fmt[tid + i * G_THREADS] = (uint8_t)fv[i];
+    if (tid < n_slots) s_fmt[tid] = (uint8_t)fv0;
+    for (int i = tid + G_THREADS; i < n_slots; i += G_THREADS) s_fmt[i] = fmt[i];   // pools over 256 slots
     if constexpr (RVPL != 0) {
 #pragma unroll
         for (int j = 0; j < RT; ++j) {               // one wavefront per token
@@ -488,7 +486,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
             uint32_t key[RVPL];
 #pragma unroll
             for (int i = 0; i < RVPL; ++i)
-                key[i] = (i * MOE_WAVE + lane < E && (L.mask == nullptr || mk[i] != 0)) ? route_ord(lg[j][i]) : 0u;
+                key[i] = (i * MOE_WAVE + lane < E && mk[i] != 0) ? route_ord(lg[j][i]) : 0u;
             int id;
             float wt;
             const int found = route_select<RVPL>(key, k, id, wt);
@@ -602,7 +600,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
 // FUSE 0: the block tables come from a separate align launch. FUSE 1: the
 // pairs are sorted here from the route results (layer_prologue). FUSE 2: the
 // tokens are routed here too (route_select<RVPL>).
-template <int FUSE, int RVPL>
+template <int FUSE, int RVPL, int RT>
 __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     SlotView pool, int n_slots, const uint16_t* __restrict__ x, int T, int k,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
@@ -661,7 +659,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             p1_issue_w(WA, pool, s_slot[0], 1, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
     } else {
-        const P1Range R = layer_prologue<RVPL>(L, pool.fmt, n_slots, T, k, ntile, s_fmt, s_slot, s_pr);
+        const P1Range R = layer_prologue<RVPL, RT>(L, pool.fmt, n_slots, T, k, ntile, s_fmt, s_slot, s_pr);
         u_begin = R.u_begin;
         u_end = R.u_end;
         b_first = R.b_first;
@@ -1162,7 +1160,7 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
     const int pipe_units = nb * (I / P1_ROWS);
     const int per = (pipe_units + pipe_grid - 1) / pipe_grid;
     if (BM == 16 && H <= 128 * G_WAVES * P1_G && per / (I / P1_ROWS) + 2 <= P1_MAXB) {
-        MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<0, 0>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
+        MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<0, 0, 1>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
                    sv, n_slots, x, T, k, sorted_pair, block_slot, n_padded, H, I, hbuf, LayerIO{});
     } else {
         MOE_LAUNCH(K_GEMM1_STREAM, stream, gemm1_stream_kernel<BM>, dim3(units), dim3(G_THREADS), 0, stream, sv,
@@ -1204,12 +1202,21 @@ bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
     return per / (I / P1_ROWS) + 2 <= P1_MAXB;
 }
 
-template <int RVPL>
+template <int RVPL, int RT>
 static void launch_gemm1_layer(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, int H, int I,
                                uint16_t* hbuf, const LayerIO& L, hipStream_t stream) {
-    MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<RVPL == 0 ? 1 : 2, RVPL>), dim3(2 * device_cus()),
+    MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<RVPL == 0 ? 1 : 2, RVPL, RT>), dim3(2 * device_cus()),
                dim3(G_THREADS), 0, stream, sv, n_slots, x, T, k, (const int32_t*)nullptr, (const int32_t*)nullptr,
                (const int32_t*)nullptr, H, I, hbuf, L);
+}
+
+// routing inside the gate/up kernel: RT tokens per wavefront, 64 * VPL experts
+template <int VPL>
+static void launch_gemm1_route(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, int H, int I,
+                               uint16_t* hbuf, const LayerIO& L, hipStream_t stream) {
+    if (T <= G_WAVES) launch_gemm1_layer<VPL, 1>(sv, n_slots, x, T, k, H, I, hbuf, L, stream);
+    else if (T <= 2 * G_WAVES) launch_gemm1_layer<VPL, 2>(sv, n_slots, x, T, k, H, I, hbuf, L, stream);
+    else launch_gemm1_layer<VPL, 4>(sv, n_slots, x, T, k, H, I, hbuf, L, stream);
 }
 
 hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const uint8_t* mask,
@@ -1227,17 +1234,14 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
     uint16_t* hbuf = (uint16_t*)ws;
     float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
     LayerIO L{logits, mask, slot_of_expert, E, ids, w, sorted_pair, block_slot, counts, seg_offset, n_padded, err};
-    if (T <= LAYER_ROUTE_MAX_T) {
-        if (E <= 64) launch_gemm1_layer<1>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
-        else if (E <= 128) launch_gemm1_layer<2>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
-        else if (E <= 256) launch_gemm1_layer<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
-        else if (E <= 512) launch_gemm1_layer<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
-        else launch_gemm1_layer<16>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+    if (T <= LAYER_ROUTE_MAX_T && E <= 512) {
+        if (E <= 256) launch_gemm1_route<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        else launch_gemm1_route<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
     } else {
         hipError_t e = launch_route(logits, mask, T, E, k, ids, w, err, stream);
         if (e != hipSuccess) return e;
         L.logits = nullptr;
-        launch_gemm1_layer<0>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
+        launch_gemm1_layer<0, 1>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
