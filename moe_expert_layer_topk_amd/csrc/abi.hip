@@ -203,8 +203,12 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
 }
 
 size_t moe_layer_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode) {
-    const size_t ffn = moe_ffn_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode);
+    size_t ffn = moe_ffn_workspace_bytes(T, k, E, hidden, inter, block_m, act_mode);
     if (ffn == 0) return 0;
+    if (act_mode == MOE_ACT_BF16 && block_m == 16) {          // the decode layer path's larger need
+        const size_t lay = moe::layer_stream_workspace_bytes(T, k, hidden, inter, capacity(T, k, E, block_m));
+        ffn = ffn > lay ? ffn : lay;
+    }
     return up256(moe_route_align_workspace_bytes(T, k, E, block_m)) + ffn;
 }
 

@@ -418,6 +418,9 @@ struct LayerIO {
     int32_t* seg_offset;
     int32_t* n_padded;
     int32_t* err;                   // [0] route, [1] align
+    int4* gdesc;                    // written by workgroup 0 for the down kernel's grid2 workgroups:
+    int grid2;                      //   (first unit, end unit, first slot, its format)
+    int H;
 };
 
 struct P1Range { int u_begin, u_end, b_first, nblk; };
@@ -430,6 +433,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_off[MOE_MAX_E];
     __shared__ int s_ids[LAYER_MAX_NP];
+    __shared__ int s_sl[MOE_MAX_E];                   // slot of each expert
     __shared__ int s_wsum[G_WAVES];
     const int tid = threadIdx.x, lane = lane_id(), wv = tid / MOE_WAVE;
     const int NP = T * k, E = L.E;
@@ -474,6 +478,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         if (e < E) {
             s_tok[e] = 0ull;
             s_cnt[e] = 0;
+            s_sl[e] = slot_e[i];
         }
     }
     if (tid < n_slots) s_fmt[tid] = (uint8_t)fv0;
@@ -584,6 +589,30 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         for (int b = b0; b < b1; ++b) s_slot[b - R.b_first] = slot_e[i];
     }
     __syncthreads();                                   // sentinels before the pairs
+    if (writer && L.gdesc) {
+        // the down kernel's unit ranges (its units: block x 64 hidden rows)
+        // with the slot and format of each range's first block, so that it
+        // loads its first weights without waiting for these tables
+        const int ntile2 = L.H / 64;
+        const int n_units2 = (total / 16) * ntile2;
+        const int per2 = (n_units2 + L.grid2 - 1) / L.grid2;
+        for (int g = tid; g < L.grid2; g += G_THREADS) {
+            const int ub = g * per2, ue = min(n_units2, ub + per2);
+            int slot = -1, f = 0;
+            if (ub < ue) {
+                const int pos = (ub / ntile2) * 16;
+                int lo = 0, hi = E - 1;                // last expert whose segment starts at or before pos
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_off[mid] <= pos) lo = mid;
+                    else hi = mid - 1;
+                }
+                slot = s_sl[lo];
+                f = slot >= 0 ? s_fmt[slot] : 0;
+            }
+            L.gdesc[g] = make_int4(ub, ue, slot, f);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int p = tid + j * G_THREADS, e = pid[j];
@@ -921,11 +950,15 @@ __device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, bool 
     }
 }
 
-template <int P2_C>
+// GD: the unit range and the first block's slot and format come from the
+// descriptor the gate/up kernel wrote (whole-layer call), so the first
+// weights are loaded in the same round trip as the tables.
+template <int P2_C, bool GD>
 __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
-    const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf) {
+    const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf,
+    const int4* __restrict__ gdesc) {
     __shared__ uint8_t s_fmt[MOE_MAX_SLOTS];
     __shared__ int s_slot[P2_MAXB];
     __shared__ int s_pr[P2_MAXB][16];
@@ -934,27 +967,61 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     const int ntile = H / G2_COLS;
     const int chunks = I / 64;
     const int groups = I / MOE_INT4_G;
-    const int n_units = (*n_padded / 16) * ntile;
-    const int per = (n_units + gridDim.x - 1) / gridDim.x;
-    const int u_begin = blockIdx.x * per;
-    const int u_end = min(n_units, u_begin + per);
+    int u_begin, u_end, g_slot = -1, g_fmt = 0;
+    if constexpr (GD) {
+        const int4 d = gdesc[blockIdx.x];
+        u_begin = __builtin_amdgcn_readfirstlane(d.x);
+        u_end = __builtin_amdgcn_readfirstlane(d.y);
+        g_slot = __builtin_amdgcn_readfirstlane(d.z);
+        g_fmt = __builtin_amdgcn_readfirstlane(d.w);
+    } else {
+        const int n_units = (*n_padded / 16) * ntile;
+        const int per = (n_units + gridDim.x - 1) / gridDim.x;
+        u_begin = blockIdx.x * per;
+        u_end = min(n_units, u_begin + per);
+    }
     const int b_first = u_begin / ntile;
     const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
-    for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
-    for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
-        const int bb = i / 17, r = i % 17;
-        if (r == 16) s_slot[bb] = block_slot[b_first + bb];
-        else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
-    }
-    __syncthreads();
-    if (nblk == 0) return;
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
-
     P2W<P2_C> WA, WB;
     P2H<P2_C> Hh;
     int hblock = -1;
     float wt = 0.f;
-    {
+    if constexpr (GD) {
+        if (nblk == 0) return;                       // uniform over the workgroup
+        // the tables, then the first unit's weights, in one round trip (loads
+        // complete in issue order: the tables can be waited for while the
+        // weights stay in flight; a non-resident first block reads slot 0's
+        // bytes and ignores them)
+        const int i0 = threadIdx.x, i1 = threadIdx.x + G_THREADS;
+        int f0 = 0, d0 = 0, d1 = 0;
+        if (i0 < n_slots) f0 = pool.fmt[i0];
+        if (i0 < nblk * 17) d0 = i0 % 17 == 16 ? block_slot[b_first + i0 / 17] : sorted_pair[(b_first + i0 / 17) * 16 + i0 % 17];
+        if (i1 < nblk * 17) d1 = i1 % 17 == 16 ? block_slot[b_first + i1 / 17] : sorted_pair[(b_first + i1 / 17) * 16 + i1 % 17];
+        __builtin_amdgcn_sched_barrier(0);
+        p2_issue_w(WA, pool, max(g_slot, 0), (g_fmt == 1 && I % MOE_INT4_G == 0) ? 1 : 0,
+                   (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0 < n_slots) s_fmt[i0] = (uint8_t)f0;
+        if (i0 < nblk * 17) {
+            if (i0 % 17 == 16) s_slot[i0 / 17] = d0;
+            else s_pr[i0 / 17][i0 % 17] = d0;
+        }
+        if (i1 < nblk * 17) {
+            if (i1 % 17 == 16) s_slot[i1 / 17] = d1;
+            else s_pr[i1 / 17][i1 % 17] = d1;
+        }
+        for (int i = i1; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];       // pools over 256 slots
+        barrier_lds();                               // tables written; the weight loads stay in flight
+    } else {
+        for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
+        for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
+            const int bb = i / 17, r = i % 17;
+            if (r == 16) s_slot[bb] = block_slot[b_first + bb];
+            else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
+        }
+        __syncthreads();
+        if (nblk == 0) return;
         const int s0 = s_slot[0];
         if (s0 >= 0) p2_issue_w(WA, pool, s0, fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
     }
@@ -1129,18 +1196,27 @@ size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
 template <int BM>
 static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, const float* topk_w,
                                 const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
-                                int cap, int H, int I, const uint16_t* hbuf, float* ybuf, hipStream_t stream) {
+                                int cap, int H, int I, const uint16_t* hbuf, float* ybuf, hipStream_t stream,
+                                const int4* gdesc = nullptr) {
     const int NP = T * k;
     const int nb = cap / BM;
     const int pipe_grid = 2 * device_cus();
     const int units2 = nb * (H / G2_COLS);
     const int per2 = (units2 + pipe_grid - 1) / pipe_grid;
     if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
-        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel<8>, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
-                   n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+        if (gdesc)
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, true>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
+                       sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
+        else
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, false>), dim3(pipe_grid), dim3(G_THREADS), 0,
+                       stream, sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
     } else if (BM == 16 && I <= 64 * 12 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
-        MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_pipe_kernel<12>, dim3(pipe_grid), dim3(G_THREADS), 0, stream, sv,
-                   n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
+        if (gdesc)
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<12, true>), dim3(pipe_grid), dim3(G_THREADS), 0,
+                       stream, sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
+        else
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<12, false>), dim3(pipe_grid), dim3(G_THREADS), 0,
+                       stream, sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
     } else {
         MOE_LAUNCH(K_GEMM2_STREAM, stream, gemm2_stream_kernel<BM>, dim3(units2), dim3(G_THREADS), 0, stream, sv,
                    n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf);
@@ -1194,6 +1270,10 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
 }
 
 // ------------------------------------------------------------ whole layer
+size_t layer_stream_workspace_bytes(int T, int k, int H, int I, int cap) {
+    return stream_workspace_bytes(T, k, H, I, cap) + up256((size_t)16 * 2 * device_cus());
+}
+
 bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
     if (block_m != 16 || T > LAYER_MAX_T || T * k > LAYER_MAX_NP || E > MOE_MAX_E) return false;
     if (H > 128 * G_WAVES * P1_G) return false;
@@ -1233,7 +1313,9 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
     const int H = pa.hidden, I = pa.inter;
     uint16_t* hbuf = (uint16_t*)ws;
     float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
-    LayerIO L{logits, mask, slot_of_expert, E, ids, w, sorted_pair, block_slot, counts, seg_offset, n_padded, err};
+    int4* gdesc = (int4*)((uint8_t*)ws + stream_workspace_bytes(T, k, H, I, cap));
+    LayerIO L{logits, mask,     slot_of_expert, E,          ids,         w,          sorted_pair,
+              block_slot, counts, seg_offset, n_padded, err, gdesc, 2 * device_cus(), H};
     if (T <= LAYER_ROUTE_MAX_T && E <= 512) {
         if (E <= 256) launch_gemm1_route<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
         else launch_gemm1_route<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
@@ -1246,7 +1328,7 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_gemm2_stream<16>(sv, pa.n_slots, T, k, w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf,
-                            stream);
+                            stream, gdesc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_combine_f32(ybuf, w, T, k, H, out, stream);

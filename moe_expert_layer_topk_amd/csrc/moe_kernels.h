@@ -58,6 +58,7 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream);
 // whole decode layer (route and align inside the gate/up kernel); layer_stream_ok says where it applies
 bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap);
+size_t layer_stream_workspace_bytes(int T, int k, int H, int I, int cap);
 hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const uint8_t* mask,
                                const int32_t* slot_of_expert, int E, const uint16_t* x, int T, int k, int32_t* ids,
                                float* w, int32_t* sorted_pair, int32_t* block_slot, int32_t* counts,
