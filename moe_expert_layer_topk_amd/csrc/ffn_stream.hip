@@ -92,6 +92,21 @@ constexpr int G2_COLS = 64;   // hidden rows per gemm2 unit
 constexpr int G2_MAXC = 8;    // 64-wide K chunks per wave issued together
 constexpr int STREAM_MAX_T = 64;
 
+// Unit ranges of the persistent decode kernels (grid G, even: two workgroups
+// per CU). Workgroups b and b + G/2 split one contiguous range of
+// ceil(n / (G/2)) units in halves, the first half to b, so every workgroup
+// holds within one unit of every other (with ceil(n / G) units each, the
+// grid's last workgroups were left with short or empty ranges).
+__host__ __device__ inline int pair_units(int n, int G) { return (n + G / 2 - 1) / (G / 2); }
+__host__ __device__ inline int max_units(int n, int G) { return (pair_units(n, G) + 1) / 2; }
+__host__ __device__ inline void unit_range(int n, int G, int b, int& ub, int& ue) {
+    const int h = G / 2, pp = pair_units(n, G);
+    const int pb = min(n, (b < h ? b : b - h) * pp), pe = min(n, pb + pp);
+    const int split = pb + (pe - pb + 1) / 2;
+    ub = b < h ? pb : split;
+    ue = b < h ? split : pe;
+}
+
 
 // ------------------------------------------------------------ gemm1
 // One unit per workgroup. Round trip 1: n_padded, the block's slot and pair
@@ -576,9 +591,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
     // this workgroup's unit range and its blocks' tables
     P1Range R;
     const int n_units = (total / 16) * ntile;
-    const int per = (n_units + gridDim.x - 1) / gridDim.x;
-    R.u_begin = blockIdx.x * per;
-    R.u_end = min(n_units, R.u_begin + per);
+    unit_range(n_units, gridDim.x, blockIdx.x, R.u_begin, R.u_end);
     R.b_first = R.u_begin / ntile;
     R.nblk = R.u_begin < R.u_end ? (R.u_end - 1) / ntile - R.b_first + 1 : 0;
     for (int i = tid; i < R.nblk * 16; i += G_THREADS) s_pr[i / 16][i % 16] = NP;
@@ -595,9 +608,9 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         // loads its first weights without waiting for these tables
         const int ntile2 = L.H / 64;
         const int n_units2 = (total / 16) * ntile2;
-        const int per2 = (n_units2 + L.grid2 - 1) / L.grid2;
         for (int g = tid; g < L.grid2; g += G_THREADS) {
-            const int ub = g * per2, ue = min(n_units2, ub + per2);
+            int ub, ue;
+            unit_range(n_units2, L.grid2, g, ub, ue);
             int slot = -1, f = 0;
             if (ub < ue) {
                 const int pos = (ub / ntile2) * 16;
@@ -650,9 +663,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
     if constexpr (FUSE == 0) {
         const int n_units = (*n_padded / 16) * ntile;
-        const int per = (n_units + gridDim.x - 1) / gridDim.x;
-        u_begin = blockIdx.x * per;
-        u_end = min(n_units, u_begin + per);
+        unit_range(n_units, gridDim.x, blockIdx.x, u_begin, u_end);
         b_first = u_begin / ntile;
         nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
         if (nblk == 0) return;
@@ -745,10 +756,16 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         // u+2 writes this half only after the barrier of unit u+1, which wave
         // 0 reaches after its reads above
     };
-    for (int u = u_begin; u < u_end; u += 2) {
+    // pairs of units, then an odd last one after the loop: a path that ran
+    // one step and returned to the loop head would leave the other register
+    // set's loads pending there, and the compiler would then wait for every
+    // load in flight at the head of each iteration (the prefetch included)
+    int u = u_begin;
+    for (; u + 1 < u_end; u += 2) {
         step(u, WA, WB);
-        if (u + 1 < u_end) step(u + 1, WB, WA);
+        step(u + 1, WB, WA);
     }
+    if (u < u_end) step(u, WA, WB);
 }
 
 // ------------------------------------------------------------ gemm2
@@ -933,20 +950,19 @@ __device__ __forceinline__ void p2_issue_w(P2W<C>& W, const SlotView& pool, int 
     W.r[C] = *(const i32x4*)(fmt ? sz4 : sc8);
 }
 
-// h row of this lane's position in the K order of the block's W2 layout
-// (zero for a padding position)
+// h row of this lane's position in the K order of the block's W2 layout, with
+// no branch around the loads (chunks past the row repeat its last one,
+// unused). A padding position reads the block's first row (always a real
+// pair; the same lines as lane 0): it only feeds that position's output
+// column, which is never stored.
 template <int C>
-__device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, bool valid, int fmt, int q, int chunks) {
+__device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, int fmt, int q, int chunks) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
+    for (int i = 0; i < C; ++i) {
+        const int c = min(i, chunks - 1);
         const int k0 = fmt ? (c >> 1) * 128 + q * 32 + (c & 1) * 16 : c * 64 + q * 16;
-        if (c < chunks && valid) {
-            Hh.v[c][0] = *(const i32x4*)(hr + k0);
-            Hh.v[c][1] = *(const i32x4*)(hr + k0 + 8);
-        } else {
-            Hh.v[c][0] = i32x4{0, 0, 0, 0};
-            Hh.v[c][1] = i32x4{0, 0, 0, 0};
-        }
+        Hh.v[i][0] = *(const i32x4*)(hr + k0);
+        Hh.v[i][1] = *(const i32x4*)(hr + k0 + 8);
     }
 }
 
@@ -976,9 +992,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         g_fmt = __builtin_amdgcn_readfirstlane(d.w);
     } else {
         const int n_units = (*n_padded / 16) * ntile;
-        const int per = (n_units + gridDim.x - 1) / gridDim.x;
-        u_begin = blockIdx.x * per;
-        u_end = min(n_units, u_begin + per);
+        unit_range(n_units, gridDim.x, blockIdx.x, u_begin, u_end);
     }
     const int b_first = u_begin / ntile;
     const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
@@ -1023,7 +1037,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         __syncthreads();
         if (nblk == 0) return;
         const int s0 = s_slot[0];
-        if (s0 >= 0) p2_issue_w(WA, pool, s0, fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        p2_issue_w(WA, pool, max(s0, 0), fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
     }
     auto step = [&](int u, P2W<P2_C>& Wc, P2W<P2_C>& Wn) {
         const int bb = u / ntile - b_first;
@@ -1032,14 +1046,22 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != hblock) {              // new block: its h rows and route weights
-            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + m) * I, valid, fmt_of(slot), q, chunks);
-            wt = valid ? topk_w[pr] : 0.f;
+            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + (valid ? m : 0)) * I, fmt_of(slot), q, chunks);
+            wt = topk_w[valid ? pr : 0];              // (used only where valid)
             hblock = bb;
         }
-        if (u + 1 < u_end) {
-            const int sn = s_slot[(u + 1) / ntile - b_first];
-            if (sn >= 0) p2_issue_w(Wn, pool, sn, fmt_of(sn), ((u + 1) % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        {
+            // the next unit's weights, with no branch around the loads (slot 0
+            // for a non-resident expert, whose unit ignores them; past the
+            // range: this unit again), so the compiler's count of loads in
+            // flight stays exact and the wait below leaves them in flight
+            const int un = min(u + 1, u_end - 1);
+            const int sn = s_slot[un / ntile - b_first];
+            p2_issue_w(Wn, pool, max(sn, 0), fmt_of(sn), (un % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
         }
+        // every path waits here for this unit's weight loads, so no load into
+        // a register set is still pending when the set is refilled
+        p2_landed(Wc);
         float* yrow = ybuf + (size_t)(valid ? pr : 0) * H + n0 + 4 * q;
         if (slot < 0) {                               // non-resident expert: its pairs add zero
             if (valid) *(f32x4*)yrow = f32x4{0, 0, 0, 0};
@@ -1085,10 +1107,16 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         }
         if (valid) *(f32x4*)yrow = acc * wt;
     };
-    for (int u = u_begin; u < u_end; u += 2) {
+    // pairs of units, then an odd last one after the loop: a path that ran
+    // one step and returned to the loop head would leave the other register
+    // set's loads pending there, and the compiler would then wait for every
+    // load in flight at the head of each iteration (the prefetch included)
+    int u = u_begin;
+    for (; u + 1 < u_end; u += 2) {
         step(u, WA, WB);
-        if (u + 1 < u_end) step(u + 1, WB, WA);
+        step(u + 1, WB, WA);
     }
+    if (u < u_end) step(u, WA, WB);
 }
 
 // ------------------------------------------------------------ combine
@@ -1202,7 +1230,7 @@ static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, c
     const int nb = cap / BM;
     const int pipe_grid = 2 * device_cus();
     const int units2 = nb * (H / G2_COLS);
-    const int per2 = (units2 + pipe_grid - 1) / pipe_grid;
+    const int per2 = max_units(units2, pipe_grid);
     if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
         if (gdesc)
             MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, true>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
@@ -1234,7 +1262,7 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
     // the pipelined kernel: 16-pair blocks, hidden <= 2048, and each workgroup's
     // unit range must span at most P1_MAXB blocks (always true unless the grid is tiny)
     const int pipe_units = nb * (I / P1_ROWS);
-    const int per = (pipe_units + pipe_grid - 1) / pipe_grid;
+    const int per = max_units(pipe_units, pipe_grid);
     if (BM == 16 && H <= 128 * G_WAVES * P1_G && per / (I / P1_ROWS) + 2 <= P1_MAXB) {
         MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<0, 0, 1>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
                    sv, n_slots, x, T, k, sorted_pair, block_slot, n_padded, H, I, hbuf, LayerIO{});
@@ -1278,7 +1306,7 @@ bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
     if (block_m != 16 || T > LAYER_MAX_T || T * k > LAYER_MAX_NP || E > MOE_MAX_E) return false;
     if (H > 128 * G_WAVES * P1_G) return false;
     const int pipe_grid = 2 * device_cus();
-    const int per = ((cap / 16) * (I / P1_ROWS) + pipe_grid - 1) / pipe_grid;
+    const int per = max_units((cap / 16) * (I / P1_ROWS), pipe_grid);
     return per / (I / P1_ROWS) + 2 <= P1_MAXB;
 }
 
