@@ -142,12 +142,16 @@ __device__ __forceinline__ i32x8 frag_read(const uint8_t* st, int r, int o0, int
 }
 
 // max over each row of 16 lanes (quad swaps, then row rotations by 4 and 8)
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true)));
-    return v;
+// of non-negative values, as integers: the bit patterns of non-negative
+// floats order like the floats, and an integer max takes its DPP operand
+// directly (a float max would first canonicalise the moved value)
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+    int x = __float_as_int(v);
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, true));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));
+    return __int_as_float(x);
 }
 
 // two fp32 -> packed bf16, round to nearest even (hardware conversion)
@@ -155,8 +159,6 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// silu with the hardware reciprocal (about 1 ulp)
-__device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------ prep
 // Block 0 lists, in order, the FP8 tiles (pairs of consecutive blocks of one
@@ -470,6 +472,16 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
             float* s_amax = (float*)(smem + MM_AMAX);
             const f32x4 sg = *(const f32x4*)(md + 4 * (nw * 64 + 4 * m));
             const f32x4 su = *(const f32x4*)(md + 512 + 4 * (nw * 64 + 4 * m));
+            // with z = g sg (g, u: gate and up accumulators, sg, su: row
+            // scales), h = silu(z) (u su) = (g u) (sg su) / (1 + 2^(g (-sg log2 e))):
+            // two column constants, so an element costs four multiplies, an
+            // add, one exp2 and one reciprocal
+            f32x4 ce, ch;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                ce[n] = sg[n] * -1.44269504088896341f;
+                ch[n] = sg[n] * su[n];
+            }
             // h replaces the gate accumulators
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -478,11 +490,13 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                     float mx = 0.f;
 #pragma unroll
                     for (int n = 0; n < 4; ++n) {
-                        const float h = silu_rcp(acc[a][n][i] * sg[n]) * (acc[a][n + 4][i] * su[n]);
+                        const float g = acc[a][n][i];
+                        const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * ce[n]));
+                        const float h = (g * ch[n]) * acc[a][n + 4][i] * r;
                         acc[a][n][i] = h;
                         mx = fmaxf(mx, fabsf(h));
                     }
-                    mx = row16_max(mx);
+                    mx = row16_max_nonneg(mx);
                     if (m == 0) s_amax[nw * MM_TM + 64 * mw + 16 * a + 4 * q + i] = mx;
                 }
             barrier_lds();
