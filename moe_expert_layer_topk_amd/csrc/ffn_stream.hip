@@ -499,25 +499,29 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
     if (tid < n_slots) s_fmt[tid] = (uint8_t)fv0;
     for (int i = tid + G_THREADS; i < n_slots; i += G_THREADS) s_fmt[i] = fmt[i];   // pools over 256 slots
     if constexpr (RVPL != 0) {
+        // the wavefront's RT tokens (wv + 4 j) selected together; a token
+        // past T has no keys and gains no choices
+        uint32_t key[RT][RVPL];
 #pragma unroll
-        for (int j = 0; j < RT; ++j) {               // one wavefront per token
-            const int t = wv + j * G_WAVES;
-            if (t >= T) break;                       // uniform over the wave
-            uint32_t key[RVPL];
+        for (int j = 0; j < RT; ++j)
 #pragma unroll
             for (int i = 0; i < RVPL; ++i)
-                key[i] = (i * MOE_WAVE + lane < E && mk[i] != 0) ? route_ord(lg[j][i]) : 0u;
-            int id;
-            float wt;
-            const int found = route_select<RVPL>(key, k, id, wt);
+                key[j][i] = (wv + j * G_WAVES < T && i * MOE_WAVE + lane < E && mk[i] != 0) ? route_ord(lg[j][i]) : 0u;
+        int id[RT], found[RT];
+        float wt[RT];
+        route_select_multi<RVPL, RT>(key, k, id, wt, found);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            const int t = wv + j * G_WAVES;
+            if (t >= T) break;                       // uniform over the wave
             if (lane < k) {
-                s_ids[t * k + lane] = id;
+                s_ids[t * k + lane] = id[j];
                 if (writer) {
-                    L.ids[t * k + lane] = id;
-                    L.w[t * k + lane] = wt;
+                    L.ids[t * k + lane] = id[j];
+                    L.w[t * k + lane] = wt[j];
                 }
             }
-            if (writer && lane == 0 && found < k) atomicAdd(&L.err[0], 1);
+            if (writer && lane == 0 && found[j] < k) atomicAdd(&L.err[0], 1);
         }
     }
     __syncthreads();

@@ -58,64 +58,102 @@ __device__ __forceinline__ void route_keys(const float* __restrict__ row, const 
         key[i] = (i * MOE_WAVE + lane < E && (mask == nullptr || mk[i] != 0)) ? route_ord(v[i]) : 0u;
 }
 
-// Lane r < found returns choice r in (id, weight); lanes >= found return
-// (-1, 0). Each round takes the largest logit image; among equal images the
-// lowest expert id (lowest i, then lowest lane) wins. Each lane keeps its own
-// largest key and index, so a round is one wave-wide max plus, when a single
-// lane holds it, one lane read. Whole wave must call; key is consumed.
-template <int VPL>
-__device__ __forceinline__ int route_select(uint32_t (&key)[VPL], int k, int& my_id, float& my_w) {
+// NT tokens at once (their selection chains interleave, so a round costs
+// little more than one token's). For token n, lane r < found[n] returns
+// choice r in (my_id[n], my_w[n]); lanes >= found[n] return (-1, 0). Each
+// round takes the largest logit image; among equal images the lowest expert
+// id (lowest i, then lowest lane) wins. Each lane keeps its own largest key
+// and index, so a round is one wave-wide max plus, when a single lane holds
+// it, one lane read. A token whose keys run out (all 0) stops gaining
+// choices. Whole wave must call; key is consumed.
+template <int VPL, int NT>
+__device__ __forceinline__ void route_select_multi(uint32_t (&key)[NT][VPL], int k, int (&my_id)[NT],
+                                                   float (&my_w)[NT], int (&found)[NT]) {
     const int lane = lane_id();
-    // this lane's largest key and the lowest index holding it
-    uint32_t lb = 0;
-    int li = 0;
-    auto local_max = [&]() __attribute__((always_inline)) {
-        lb = key[0];
-        li = 0;
+    uint32_t lb[NT], my_ord[NT];
+    int li[NT];
+    // this lane's largest key of token n and the lowest index holding it
+    auto local_max = [&](int n) __attribute__((always_inline)) {
+        lb[n] = key[n][0];
+        li[n] = 0;
 #pragma unroll
         for (int i = 1; i < VPL; ++i) {
-            const bool gt = key[i] > lb;
-            lb = gt ? key[i] : lb;
-            li = gt ? i : li;
+            const bool gt = key[n][i] > lb[n];
+            lb[n] = gt ? key[n][i] : lb[n];
+            li[n] = gt ? i : li[n];
         }
     };
-    local_max();
-    uint32_t my_ord = 0;
-    my_id = -1;
-    int found = 0;
-    for (int r = 0; r < k; ++r) {
-        const uint32_t best = wave_max_u32_dpp(lb);
-        if (best == 0) break;                            // uniform across the wave
-        const uint64_t at = __ballot(lb == best);
-        int sel;
-        if (__popcll(at) == 1) {                         // one lane holds the maximum: its lowest index
-            const int wl = (int)__builtin_ctzll(at);
-            sel = __builtin_amdgcn_readlane(li, wl) * MOE_WAVE + wl;
-        } else {                                         // equal keys in several lanes: lowest expert id
-            sel = -1;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const uint64_t bi = __ballot(key[i] == best);
-                if (sel < 0 && bi != 0) sel = i * MOE_WAVE + (int)__builtin_ctzll(bi);
+    for (int n = 0; n < NT; ++n) {
+        local_max(n);
+        my_ord[n] = 0;
+        my_id[n] = -1;
+        found[n] = 0;
+    }
+    for (int r = 0; r < k; ++r) {
+        uint32_t best[NT];
+        int sel[NT];
+        bool tie = false;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) best[n] = wave_max_u32_dpp(lb[n]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const uint64_t at = __ballot(lb[n] == best[n]);      // not empty: some lane holds best
+            const int wl = (int)__builtin_ctzll(at);
+            sel[n] = best[n] == 0 ? -1 : __builtin_amdgcn_readlane(li[n], wl) * MOE_WAVE + wl;
+            tie = tie || (best[n] != 0 && __popcll(at) > 1);
+        }
+        if (tie) {                                              // uniform; rare
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {                      // equal keys in several lanes: lowest expert id
+                if (best[n] == 0) continue;
+                int s2 = -1;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const uint64_t bi = __ballot(key[n][i] == best[n]);
+                    if (s2 < 0 && bi != 0) s2 = i * MOE_WAVE + (int)__builtin_ctzll(bi);
+                }
+                sel[n] = s2;
             }
         }
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) key[i] = (i * MOE_WAVE + lane == sel) ? 0u : key[i];
-        local_max();                                     // changes only the winner lane's (lb, li)
-        if (lane == r) {
-            my_ord = best;
-            my_id = sel;
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) key[n][i] = (i * MOE_WAVE + lane == sel[n]) ? 0u : key[n][i];
+            local_max(n);                                       // changes only the winner lane's (lb, li)
+            if (lane == r && best[n] != 0) {
+                my_ord[n] = best[n];
+                my_id[n] = sel[n];
+            }
+            found[n] += best[n] != 0 ? 1 : 0;
         }
-        ++found;
     }
-    const float my_logit = route_ord_value(my_ord);
-    const float top = __shfl(my_logit, 0, 64);
-    const float z = (lane < found) ? expf(my_logit - top) : 0.f;
-    float s = 0.f;
-    for (int r = 0; r < found; ++r) s += __shfl(z, r, 64);   // fixed order
-    my_w = (lane < found) ? z / s : 0.f;
-    if (lane >= found) my_id = -1;
-    return found;
+    // softmax over the chosen logits, summed in fixed order (choices past
+    // found[n] add exact zeros)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float my_logit = route_ord_value(my_ord[n]);
+        const float top = __shfl(my_logit, 0, 64);
+        const float z = (lane < found[n]) ? expf(my_logit - top) : 0.f;
+        float s = 0.f;
+        for (int r = 0; r < found[n]; ++r) s += __shfl(z, r, 64);
+        my_w[n] = (lane < found[n]) ? z / s : 0.f;
+        if (lane >= found[n]) my_id[n] = -1;
+    }
+}
+
+// One token (see route_select_multi).
+template <int VPL>
+__device__ __forceinline__ int route_select(uint32_t (&key)[VPL], int k, int& my_id, float& my_w) {
+    uint32_t kk[1][VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) kk[0][i] = key[i];
+    int id[1], found[1];
+    float w[1];
+    route_select_multi<VPL, 1>(kk, k, id, w, found);
+    my_id = id[0];
+    my_w = w[0];
+    return found[0];
 }
 
 // One token: route_keys then route_select.
