@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restri
     const long it = live ? item : 0;                    // idle lanes redo item 0 and store nothing
     const int r = (int)(it / groups), g = (int)(it % groups);
     const size_t off = (size_t)r * cols + g * MOE_ACT_G + 8 * (lane & 15);
-    const i32x4 raw = *(const i32x4*)(x + off);
+    const i32x4 raw = __builtin_nontemporal_load((const i32x4*)(x + off));   // read once
     float v[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {

@@ -1144,8 +1144,14 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(const YT* __restrict_
             for (int j = 0; j < KMAX; ++j) {
                 if (j < k) {
                     const YT* row = ybuf + ((size_t)t * k + j) * H + c;
-                    v[j][0] = *(const i32x4*)row;
-                    if constexpr (sizeof(YT) == 4) v[j][1] = *(const i32x4*)(row + 4);
+                    if constexpr (sizeof(YT) == 4) {
+                        v[j][0] = *(const i32x4*)row;
+                        v[j][1] = *(const i32x4*)(row + 4);
+                    } else {
+                        // batched sizes: the weighted pair rows are read once,
+                        // and stream past the caches
+                        v[j][0] = __builtin_nontemporal_load((const i32x4*)row);
+                    }
                 }
             }
 #pragma unroll
