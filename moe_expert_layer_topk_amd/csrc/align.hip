@@ -72,14 +72,28 @@ __device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_tmp, i
         s_off[e] = off;
         counts[e] = c;
         seg_offset[e] = off;
-        int slot = slot_of_expert[e];
-        for (int b = off / block_m; b < (off + padded) / block_m; ++b) block_slot[b] = slot;
-        for (int q = off + c; q < off + padded; ++q) sorted_pair[q] = sentinel;
-        if (slot < 0 && c > 0) atomicAdd(err, c);
+        if (slot_of_expert[e] < 0 && c > 0) atomicAdd(err, c);
     }
     if (e == 0) {
         seg_offset[E] = total;
         *n_padded = total;
+    }
+    __syncthreads();
+    // block -> slot and the sentinel tails, spread over the workgroup by
+    // block (a hot expert's segment spans many blocks): a block's expert is
+    // the last one whose segment starts at or before it (empty segments
+    // share their offset with the next expert, so the last one is never
+    // empty); only a segment's last block holds padding
+    for (int b = threadIdx.x; b < total / block_m; b += blockDim.x) {
+        const int pos = b * block_m;
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= pos) lo = mid;
+            else hi = mid - 1;
+        }
+        block_slot[b] = slot_of_expert[lo];
+        for (int q = max(pos, s_off[lo] + s_cnt[lo]); q < pos + block_m; ++q) sorted_pair[q] = sentinel;
     }
     __syncthreads();
 }
@@ -168,13 +182,18 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
     __shared__ int s_off[MOE_MAX_E];
     __shared__ int s_tmp[2 * ALIGN_WAVES];
     const int e = threadIdx.x;
-    constexpr int B = 8;                 // chunk counts loaded per round trip
+    constexpr int B = 32;                // chunk counts loaded per round trip (clamped, no branches)
+    int v[B];                            // the last group read; with n_chunks <= B, all of them
+    auto read_group = [&](int b0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = hist[(size_t)min(b0 + j, n_chunks - 1) * E + e];
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = b0 + j < n_chunks ? v[j] : 0;
+    };
     if (e < E) {
         int c = 0;
         for (int b0 = 0; b0 < n_chunks; b0 += B) {
-            int v[B];
-#pragma unroll
-            for (int j = 0; j < B; ++j) v[j] = b0 + j < n_chunks ? hist[(size_t)(b0 + j) * E + e] : 0;
+            read_group(b0);
 #pragma unroll
             for (int j = 0; j < B; ++j) c += v[j];
         }
@@ -186,9 +205,7 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
     if (e < E) {                         // hist[b][e] <- start of chunk b's pairs of expert e
         int run = s_off[e];
         for (int b0 = 0; b0 < n_chunks; b0 += B) {
-            int v[B];
-#pragma unroll
-            for (int j = 0; j < B; ++j) v[j] = b0 + j < n_chunks ? hist[(size_t)(b0 + j) * E + e] : 0;
+            if (n_chunks > B) read_group(b0);
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 if (b0 + j < n_chunks) hist[(size_t)(b0 + j) * E + e] = run;
