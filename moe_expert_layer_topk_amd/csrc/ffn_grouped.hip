@@ -102,7 +102,7 @@ __device__ __forceinline__ void int4_to_e4m3_16(uint2 packed, float zero, uint32
 // ------------------------------------------------------------ gemm1
 // Tile: BM pair rows x 128 inter columns (128 gate rows + 128 up rows of W13).
 // Wave w owns inter columns [32w, 32w+32).
-template <int BM>
+template <int BM, bool ONLY4>
 __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __restrict__ xq,
                                            const uint8_t* __restrict__ xs, int NP, int k,
                                            const int32_t* __restrict__ sorted_pair,
@@ -123,8 +123,9 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
     const int slot = block_slot[mt_idx];
     if (slot < 0) return;
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int fmt = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;   // int4 needs inter % 128 == 0
-    if (int4_only && fmt == 0) return;
+    const int fmt_slot = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;   // int4 needs inter % 128 == 0
+    if (int4_only && fmt_slot == 0) return;
+    const int fmt = ONLY4 ? 1 : fmt_slot;             // (the int4-only instance has no FP8 path)
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int c0 = nt_idx * 128;                      // first inter column of the tile
     const int ncols = min(128, I - c0);               // valid inter columns
@@ -150,23 +151,24 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
 
     const uint8_t* w13 = sb;
     const uint8_t* sz13 = sb + pool.off[1][1];
-    for (int g = 0; g < groups; ++g) {
+    // K step g: every load of the step first, then the LDS writes. A: BM
+    // gathered rows x 128 bytes; B: 256 weight rows x 128 K (gate rows c0..,
+    // up rows I+c0..); int4: the codes, the zeros of the rows staged and the
+    // scales of this lane's four output columns. The loads of step g + 1 are
+    // issued once step g sits in LDS, so they fly during its matrix work.
+    constexpr int NA = (BM * 8 + GT - 1) / GT, NB = 256 * 8 / GT;
+    i32x4 va[NA];
+    i32x4 vb[NB];
+    float zb[NB];
+    float sgn[2][2] = {{0.f, 0.f}, {0.f, 0.f}};      // scales of the step being loaded
+    auto load_step = [&](int g) __attribute__((always_inline)) {
         const int k0 = g * 128;
-        // every load of the step first (one round trip), then the LDS writes.
-        // A: BM gathered rows x 128 bytes; B: 256 weight rows x 128 K (gate
-        // rows c0.., up rows I+c0..); int4: the codes, the zeros of the rows
-        // staged and the scales of this lane's four output columns
-        constexpr int NA = (BM * 8 + GT - 1) / GT, NB = 256 * 8 / GT;
-        i32x4 va[NA];
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
             const int i = threadIdx.x + u * GT;
             const int t = i < BM * 8 ? s_tok[i >> 3] : -1;
             va[u] = t >= 0 ? *(const i32x4*)(xq + (size_t)t * H + k0 + (i & 7) * 16) : i32x4{0, 0, 0, 0};
         }
-        i32x4 vb[NB];
-        float zb[NB];
-        float sgu[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             const int i = threadIdx.x + u * GT;
@@ -188,9 +190,12 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
                 for (int n = 0; n < 2; ++n) {
                     const int col = wv * 32 + n * 16 + m;
                     const int wrow = (gu ? I : 0) + c0 + (col < ncols ? col : 0);
-                    sgu[gu][n] = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).x;
+                    sgn[gu][n] = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).x;
                 }
         }
+    };
+    load_step(0);
+    for (int g = 0; g < groups; ++g) {
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
             const int i = threadIdx.x + u * GT;
@@ -208,7 +213,13 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
             }
             *(i32x4*)(sB + r * LDS_ROW + ch * 16) = v;
         }
+        float sgu[2][2];
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) sgu[gu][n] = sgn[gu][n];
         __syncthreads();
+        if (g + 1 < groups) load_step(g + 1);
         // B fragments of this wave: gate cols 32w + 16n + m, up cols likewise
         i32x8 bf[2][2];
 #pragma unroll
@@ -314,7 +325,7 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
 
 // ------------------------------------------------------------ gemm2
 // Tile: BM pair rows x 128 hidden columns; wave w owns columns [32w, 32w+32).
-template <int BM>
+template <int BM, bool ONLY4>
 __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, const float* __restrict__ topk_w,
                                            const int32_t* __restrict__ sorted_pair,
                                            const int32_t* __restrict__ block_slot,
@@ -340,7 +351,8 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
         return;
     }
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int fmt = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;   // int4 needs inter % 128 == 0
+    // int4 needs inter % 128 == 0; the int4-only instance has no FP8 path
+    const int fmt = ONLY4 ? 1 : ((pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0);
     const int hgroups = (I + MOE_ACT_G - 1) / MOE_ACT_G;
     const int wgroups = I / MOE_INT4_G;
     f32x4 acc[MT][2];
@@ -348,32 +360,62 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
     for (int a = 0; a < MT; ++a) { acc[a][0] = f32x4{0, 0, 0, 0}; acc[a][1] = f32x4{0, 0, 0, 0}; }
     const uint8_t* w2 = sb + pool.off[fmt][2];
     const uint8_t* sz2 = sb + pool.off[1][3];
-    for (int g = 0; g < hgroups; ++g) {
+    // K step g: every load of the step first (A: the block's h codes; B: 128
+    // W2 rows x 128 K, int4 with the zeros of the rows staged and the scales
+    // of this lane's two output columns), then the LDS writes; the loads of
+    // step g + 1 fly during step g's matrix work
+    constexpr int NA = BM * 8 / GT, NB = 128 * 8 / GT;
+    i32x4 va[NA];
+    i32x4 vb[NB];
+    float zb[NB];
+    float scn[2] = {0.f, 0.f};
+    auto load_step = [&](int g) __attribute__((always_inline)) {
         const int k0 = g * 128;
         const int kv = min(128, I - k0);              // valid K bytes in this step
-        for (int i = threadIdx.x; i < BM * 8; i += GT) {
-            int r = i >> 3, ch = i & 7;
-            i32x4 v = {0, 0, 0, 0};
-            if (ch * 16 < kv) v = *(const i32x4*)(hq + (size_t)(mt_idx * BM + r) * I + k0 + ch * 16);
-            *(i32x4*)(sA + r * LDS_ROW + ch * 16) = v;
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int i = threadIdx.x + u * GT, r = i >> 3, ch = i & 7;
+            va[u] = ch * 16 < kv ? *(const i32x4*)(hq + (size_t)(mt_idx * BM + r) * I + k0 + ch * 16)
+                                 : i32x4{0, 0, 0, 0};
         }
-        for (int i = threadIdx.x; i < 128 * 8; i += GT) {
-            int r = i >> 3, ch = i & 7;
-            i32x4 v = {0, 0, 0, 0};
-            if (ch * 16 < kv) {
-                if (fmt == 0) {
-                    v = *(const i32x4*)(w2 + (size_t)(n0 + r) * I + k0 + ch * 16);
-                } else {
-                    uint2 pk = *(const uint2*)(w2 + (size_t)(n0 + r) * (I / 2) + (k0 + ch * 16) / 2);
-                    float z = f16x2_at(sz2 + ((size_t)(n0 + r) * wgroups + g) * 4).y;
-                    uint32_t o[4];
-                    int4_to_e4m3_16(pk, z, o);
-                    v = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-                }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int i = threadIdx.x + u * GT, r = i >> 3, ch = i & 7;
+            if (fmt == 0) {
+                vb[u] = ch * 16 < kv ? *(const i32x4*)(w2 + (size_t)(n0 + r) * I + k0 + ch * 16) : i32x4{0, 0, 0, 0};
+            } else {
+                const uint2 pk = *(const uint2*)(w2 + (size_t)(n0 + r) * (I / 2) + (k0 + ch * 16) / 2);
+                vb[u] = i32x4{(int)pk.x, (int)pk.y, 0, 0};
+                zb[u] = f16x2_at(sz2 + ((size_t)(n0 + r) * wgroups + g) * 4).y;
             }
-            *(i32x4*)(sB + r * LDS_ROW + ch * 16) = v;
         }
+        if (fmt == 1) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                scn[n] = f16x2_at(sz2 + ((size_t)(n0 + wv * 32 + n * 16 + m) * wgroups + g) * 4).x;
+        }
+    };
+    load_step(0);
+    for (int g = 0; g < hgroups; ++g) {
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int i = threadIdx.x + u * GT;
+            *(i32x4*)(sA + (i >> 3) * LDS_ROW + (i & 7) * 16) = va[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int i = threadIdx.x + u * GT;
+            i32x4 v = vb[u];
+            if (fmt == 1) {
+                uint32_t o[4];
+                int4_to_e4m3_16(make_uint2((uint32_t)vb[u][0], (uint32_t)vb[u][1]), zb[u], o);
+                v = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+            }
+            *(i32x4*)(sB + (i >> 3) * LDS_ROW + (i & 7) * 16) = v;
+        }
+        const float sc[2] = {scn[0], scn[1]};
         __syncthreads();
+        if (g + 1 < hgroups) load_step(g + 1);
         i32x8 bf[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -394,9 +436,7 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
                     f32x4 t4 = mfma_fp8_16x16x128(af, bf[n], f32x4{0, 0, 0, 0}, sa, 127);
-                    const int col = n0 + wv * 32 + n * 16 + m;
-                    const float s = f16x2_at(sz2 + ((size_t)col * wgroups + g) * 4).x;
-                    acc[a][n] += s * t4;
+                    acc[a][n] += sc[n] * t4;
                 }
             }
         }
@@ -442,20 +482,20 @@ __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t
                                                       int int4_only, const int* __restrict__ list,
                                                       const int* __restrict__ n_list) {
     if (list == nullptr) {
-        gemm1_tile<BM>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, blockIdx.y,
+        gemm1_tile<BM, false>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, blockIdx.y,
                        blockIdx.x);
         return;
     }
     const int n = *n_list;
     for (int i = blockIdx.y; i < n; i += gridDim.y) {
-        gemm1_tile<BM>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, list[i],
+        gemm1_tile<BM, true>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, list[i],
                        blockIdx.x);
         __syncthreads();
     }
 }
 
 template <int BM>
-__global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k, const float* __restrict__ topk_w,
+__global__ void __launch_bounds__(GT, 2) gemm2_fp8_kernel(GPool pool, int NP, int k, const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ sorted_pair,
                                                       const int32_t* __restrict__ block_slot,
                                                       const int32_t* __restrict__ n_padded, int H, int I,
@@ -463,14 +503,14 @@ __global__ void __launch_bounds__(GT) gemm2_fp8_kernel(GPool pool, int NP, int k
                                                       uint16_t* __restrict__ ybuf, int int4_only,
                                                       const int* __restrict__ list, const int* __restrict__ n_list) {
     if (list == nullptr) {
-        gemm2_tile<BM>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
-                       blockIdx.y, blockIdx.x);
+        gemm2_tile<BM, false>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
+                              blockIdx.y, blockIdx.x);
         return;
     }
     const int n = *n_list;
     for (int i = blockIdx.y; i < n; i += gridDim.y) {
-        gemm2_tile<BM>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
-                       list[i], blockIdx.x);
+        gemm2_tile<BM, true>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
+                             list[i], blockIdx.x);
         __syncthreads();
     }
 }
