@@ -81,6 +81,13 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restri
 constexpr int GT = 256;         // threads per workgroup (4 waves)
 constexpr int LDS_ROW = 144;    // 128 bytes of K + 16 bytes of padding
 
+// Workgroup barrier that waits only for the wave's LDS traffic. The fence of
+// __syncthreads() also waits for every global load in flight, which would
+// drain the next K step's loads at each barrier of the step loop.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // int4 row (64 packed bytes = 128 K) -> 128 e4m3 codes of q - zero (exact for
 // integer zero points), written as 8 dwords x 4 = 128 bytes
 __device__ __forceinline__ void int4_to_e4m3_16(uint2 packed, float zero, uint32_t out[4]) {
@@ -167,7 +174,10 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
         for (int u = 0; u < NA; ++u) {
             const int i = threadIdx.x + u * GT;
             const int t = i < BM * 8 ? s_tok[i >> 3] : -1;
-            va[u] = t >= 0 ? *(const i32x4*)(xq + (size_t)t * H + k0 + (i & 7) * 16) : i32x4{0, 0, 0, 0};
+            // (loads from clamped addresses, values selected after: no branch
+            // around a load, so the loads of the next step stay in flight)
+            const i32x4 ld = *(const i32x4*)(xq + (size_t)max(t, 0) * H + k0 + (i & 7) * 16);
+            va[u] = t >= 0 ? ld : i32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -175,10 +185,11 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
             const int r = i >> 3, ch = i & 7, col = r & 127;
             const int wrow = (r < 128 ? 0 : I) + c0 + (col < ncols ? col : 0);
             if (fmt == 0) {
-                vb[u] = col < ncols ? *(const i32x4*)(w13 + (size_t)wrow * H + k0 + ch * 16) : i32x4{0, 0, 0, 0};
+                const i32x4 ld = *(const i32x4*)(w13 + (size_t)wrow * H + k0 + ch * 16);
+                vb[u] = col < ncols ? ld : i32x4{0, 0, 0, 0};
             } else {
-                const uint2 pk = col < ncols ? *(const uint2*)(w13 + (size_t)wrow * (H / 2) + (k0 + ch * 16) / 2)
-                                             : make_uint2(0u, 0u);
+                const uint2 ld = *(const uint2*)(w13 + (size_t)wrow * (H / 2) + (k0 + ch * 16) / 2);
+                const uint2 pk = col < ncols ? ld : make_uint2(0u, 0u);
                 vb[u] = i32x4{(int)pk.x, (int)pk.y, 0, 0};
                 zb[u] = f16x2_at(sz13 + ((size_t)wrow * groups + g) * 4).y;
             }
@@ -218,8 +229,8 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
         for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
             for (int n = 0; n < 2; ++n) sgu[gu][n] = sgn[gu][n];
-        __syncthreads();
-        if (g + 1 < groups) load_step(g + 1);
+        barrier_lds();
+        load_step(min(g + 1, groups - 1));           // (no branch around the loads: the last step reloads itself)
         // B fragments of this wave: gate cols 32w + 16n + m, up cols likewise
         i32x8 bf[2][2];
 #pragma unroll
@@ -251,7 +262,7 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
                     }
             }
         }
-        __syncthreads();
+        barrier_lds();
     }
 
     // epilogue: row scales, silu(gate) * up, per-(row, 128 cols) quantization
@@ -375,8 +386,9 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
             const int i = threadIdx.x + u * GT, r = i >> 3, ch = i & 7;
-            va[u] = ch * 16 < kv ? *(const i32x4*)(hq + (size_t)(mt_idx * BM + r) * I + k0 + ch * 16)
-                                 : i32x4{0, 0, 0, 0};
+            const uint8_t* src = hq + (size_t)(mt_idx * BM + r) * I + k0 + ch * 16;
+            if constexpr (ONLY4) va[u] = *(const i32x4*)src;   // inter % 128 == 0: every chunk is valid
+            else va[u] = ch * 16 < kv ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -414,8 +426,8 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
             *(i32x4*)(sB + (i >> 3) * LDS_ROW + (i & 7) * 16) = v;
         }
         const float sc[2] = {scn[0], scn[1]};
-        __syncthreads();
-        if (g + 1 < hgroups) load_step(g + 1);
+        barrier_lds();
+        load_step(min(g + 1, hgroups - 1));          // (no branch around the loads: the last step reloads itself)
         i32x8 bf[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -440,7 +452,7 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
                 }
             }
         }
-        __syncthreads();
+        barrier_lds();
     }
     // epilogue: row scale, route weight, bf16 rows staged in LDS for wide stores
     const float* s2 = (const float*)(sb + pool.off[0][3]);
