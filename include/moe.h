@@ -120,6 +120,9 @@ int moe_route_align(const float* d_logits, const uint8_t* d_mask, int T, int E, 
  *        element c of a row: low nibble of byte c/2 if c is even, else high.
  *  Dequantized: FP8 W[r][c] = e4m3(q[r][c]) * scale[r];
  *               INT4 W[r][c] = (q[r][c] - zero[r][c/128]) * scale[r][c/128].
+ *  INT4 zero points are integers in [0, 15] (stored as fp16): the kernels
+ *  form q - zero exactly as a small integer before the matrix instructions
+ *  and apply the group scale after them.
  * Rows [0, I) of w13 are the gate projection, rows [I, 2I) the up projection.
  * d_slot_fmt is a device array u8[n_slots] of MOE_FMT_* values.
  * hidden % 128 == 0, inter % 64 == 0 (INT4 slots: inter % 128 == 0). */
