@@ -302,7 +302,8 @@ constexpr int P1_MAXB = 16;      // blocks per workgroup range the LDS tables ho
 //   4q..4q+3.
 // * int4 slot: r[j] = 32 nibbles of this lane's row, K group g = 4 wv + j,
 //   elements [g 128 + q 32, +32); r[4] = (scale, zero) of the row for groups
-//   4 wv .. 4 wv + 3; r[5..8] repeat r[4] (unused).
+//   4 wv .. 4 wv + 3; r[5], r[6], r[7], r[8] = the same for the C rows
+//   4q .. 4q + 3 this lane accumulates (their scales, with no lane exchange).
 // The token rows of a block are loaded in the matching K order (p1_issue_x).
 struct P1W { i32x4 r[9]; };
 struct P1X { i32x4 v[P1_G][2][2]; };         // [group][chunk][half] of this lane's token row
@@ -325,15 +326,17 @@ __device__ __forceinline__ void p1_issue_w(P1W& W, const SlotView& pool, int slo
     const uint8_t* sc8 = sb + pool.off[0][1] + 4 * (q < 2 ? i0 + 4 * q : I + i0 + 4 * (q - 2));
     // int4 sources
     const uint8_t* wr4 = sb + pool.off[1][0] + (size_t)row * (H / 2) + q * 16;
-    const uint8_t* sz4 = sb + pool.off[1][1] + ((size_t)row * groups + min(4 * wv, groups - 1)) * 4;
+    const uint8_t* szb = sb + pool.off[1][1] + (size_t)min(4 * wv, groups - 1) * 4;
+    const uint8_t* sz4 = szb + (size_t)row * groups * 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int j = i >> 1, c = i & 1;
         const uint8_t* p8 = wr8 + min(wv + j * G_WAVES, groups - 1) * 128 + c * 64 + q * 16;
-        const uint8_t* p4 = i < 4 ? wr4 + min(4 * wv + i, groups - 1) * 64 : sz4;
+        const uint8_t* p4 = i < 4 ? wr4 + min(4 * wv + i, groups - 1) * 64
+                          : (i == 4 ? sz4 : szb + (size_t)p1_row(i0, 4 * q + i - 5, I) * groups * 4);
         W.r[i] = *(const i32x4*)(fmt ? p4 : p8);
     }
-    W.r[8] = *(const i32x4*)(fmt ? sz4 : sc8);
+    W.r[8] = *(const i32x4*)(fmt ? szb + (size_t)p1_row(i0, 4 * q + 3, I) * groups * 4 : sc8);
 }
 
 // Token row of this lane (row 0 for a padding lane: its output column is
@@ -390,7 +393,7 @@ __device__ __forceinline__ f32x4 p1_int4_mma(const P1W& W, const P1X& X, int q, 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t szr = (uint32_t)__shfl((int)sz, 4 * q + i, 64);
+            const uint32_t szr = (uint32_t)(i < 3 ? W.r[5 + i][j] : W.r[8][j]);   // C row 4q + i, group 4 wv + j
             acc[i] += (float)__builtin_bit_cast(_Float16, (uint16_t)(szr & 0xFFFFu)) * t4[i];
         }
     }
