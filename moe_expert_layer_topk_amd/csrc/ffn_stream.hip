@@ -925,8 +925,9 @@ constexpr int P2_MAXB = 16;
 //   r[C] = fp32 row scales of the C rows 4q..4q+3.
 // * int4 slot: r[g] = 32 nibbles of this lane's row, K group g, elements
 //   [g 128 + q 32, +32) (g < C / 2); r[C / 2 + g / 4] holds the row's
-//   (scale, zero) of group g at dword g % 4; the other registers repeat
-//   that area (unused).
+//   (scale, zero) of group g at dword g % 4; with C = 8, r[5..8] hold those
+//   of the C rows 4q..4q+3 the lane accumulates; otherwise the other
+//   registers repeat the row's area (unused).
 template <int C>
 struct P2W { i32x4 r[C + 1]; };
 template <int C>
@@ -947,14 +948,18 @@ __device__ __forceinline__ void p2_issue_w(P2W<C>& W, const SlotView& pool, int 
     const uint8_t* wr8 = sb + pool.off[0][2] + (size_t)(n0 + m) * I + q * 16;
     const uint8_t* sc8 = sb + pool.off[0][3] + 4 * (n0 + 4 * q);
     const uint8_t* wr4 = sb + pool.off[1][2] + (size_t)(n0 + m) * (I / 2) + q * 16;
-    const uint8_t* sz4 = sb + pool.off[1][3] + (size_t)(n0 + m) * groups * 4;
+    const uint8_t* szb = sb + pool.off[1][3];
+    const uint8_t* sz4 = szb + (size_t)(n0 + m) * groups * 4;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const uint8_t* p8 = wr8 + min(i, chunks - 1) * 64;
         const uint8_t* p4 = i < C / 2 ? wr4 + min(i, max(groups, 1) - 1) * 64 : sz4 + 16 * min(i - C / 2, NSZ - 1);
+        // C = 8 (one (scale, zero) load per row): registers 5..7 and 8 hold
+        // the (scale, zero) of the C rows 4q..4q+3 this lane accumulates
+        if (C == 8 && i >= 5) p4 = szb + (size_t)(n0 + 4 * q + i - 5) * groups * 4;
         W.r[i] = *(const i32x4*)(fmt ? p4 : p8);
     }
-    W.r[C] = *(const i32x4*)(fmt ? sz4 : sc8);
+    W.r[C] = *(const i32x4*)(fmt ? (C == 8 ? szb + (size_t)(n0 + 4 * q + 3) * groups * 4 : sz4) : sc8);
 }
 
 // h row of this lane's position in the K order of the block's W2 layout, with
@@ -1088,8 +1093,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
             acc *= __builtin_bit_cast(f32x4, Wc.r[P2_C]);
         } else {
             // (q - z) exactly in bf16, each group's scale after its matrix
-            // instructions; the scales of C rows 4q..4q+3 from the lanes that
-            // loaded those rows
+            // instructions; the scales of C rows 4q..4q+3 from this lane's
+            // registers 5..8 (C = 8) or from the lanes that loaded those rows
 #pragma unroll
             for (int g = 0; g < P2_C / 2; ++g) {
                 if (g >= groups) break;                // uniform
@@ -1107,7 +1112,9 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t szr = (uint32_t)__shfl((int)sz, 4 * q + i, 64);
+                    // C row 4q + i: its own registers at C = 8, else from the lane that loaded it
+                    const uint32_t szr = P2_C == 8 ? (uint32_t)(i < 3 ? Wc.r[5 + i][g % 4] : Wc.r[8][g % 4])
+                                                   : (uint32_t)__shfl((int)sz, 4 * q + i, 64);
                     acc[i] += (float)__builtin_bit_cast(_Float16, (uint16_t)(szr & 0xFFFFu)) * t4[i];
                 }
             }
