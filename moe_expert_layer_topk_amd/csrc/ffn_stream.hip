@@ -51,17 +51,27 @@ __device__ __forceinline__ uint32_t two_bf16(float a, float b) {
     return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-// 16 int4 values (8 bytes) -> q - zero as two bf16x8 operands
+// 16 int4 values (8 bytes) -> q - zero as two bf16x8 operands. For the
+// integer zero points the format stores, q - zero is a small integer, exact
+// in fp32 and in bf16: the bf16 is the fp32's upper half, no rounding step
+// (TRUNC; the rounding form is kept where the shorter sequence measured
+// slower: it pushed the twelve-chunk down kernel into more register spills).
+template <bool TRUNC = true>
 __device__ __forceinline__ void int4x16_to_bf16(uint2 v, float zero, bf16x8& s0, bf16x8& s1) {
-    uint32_t w[2] = {v.x, v.y};
+    const uint32_t w[2] = {v.x, v.y};
     uint32_t o[8];
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
+    for (int d = 0; d < 2; ++d) {
+        const uint32_t ev = w[d] & 0x0F0F0F0Fu;           // low nibbles (even elements) as bytes
+        const uint32_t od = (w[d] >> 4) & 0x0F0F0F0Fu;    // high nibbles (odd elements)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t byte = (w[d] >> (8 * j)) & 0xFFu;
-            o[d * 4 + j] = two_bf16((float)(byte & 0xFu) - zero, (float)(byte >> 4) - zero);
+            const float a = (float)((ev >> (8 * j)) & 0xFFu) - zero;
+            const float b = (float)((od >> (8 * j)) & 0xFFu) - zero;
+            o[d * 4 + j] = TRUNC ? __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u)
+                                 : two_bf16(a, b);
         }
+    }
     i32x4 x0 = {(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     i32x4 x1 = {(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
     s0 = __builtin_bit_cast(bf16x8, x0);
@@ -1105,7 +1115,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
                 for (int c2 = 0; c2 < 2; ++c2) {
                     const int c = g * 2 + c2;
                     bf16x8 a0, a1, h0, h1;
-                    int4x16_to_bf16(make_uint2((uint32_t)Wc.r[g][2 * c2], (uint32_t)Wc.r[g][2 * c2 + 1]), z, a0, a1);
+                    int4x16_to_bf16<P2_C == 8>(make_uint2((uint32_t)Wc.r[g][2 * c2], (uint32_t)Wc.r[g][2 * c2 + 1]), z,
+                                               a0, a1);
                     split_bf16(Hh.v[c][0], Hh.v[c][1], h0, h1);
                     t4 = mfma_bf16_16x16x32(a0, h0, t4);
                     t4 = mfma_bf16_16x16x32(a1, h1, t4);
