@@ -58,8 +58,9 @@ __device__ __forceinline__ void route_keys(const float* __restrict__ row, const 
         key[i] = (i * MOE_WAVE + lane < E && (mask == nullptr || mk[i] != 0)) ? route_ord(v[i]) : 0u;
 }
 
-// NT tokens at once (their selection chains interleave, so a round costs
-// little more than one token's). For token n, lane r < found[n] returns
+// NT tokens at once (one loop of selection rounds for all of them; measured
+// on MI355X, a round of two tokens still costs close to two single-token
+// rounds, about 700 clocks each). For token n, lane r < found[n] returns
 // choice r in (my_id[n], my_w[n]); lanes >= found[n] return (-1, 0). Each
 // round takes the largest logit image; among equal images the lowest expert
 // id (lowest i, then lowest lane) wins. Each lane keeps its own largest key
