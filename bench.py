@@ -1,13 +1,21 @@
 """Benchmark of the MoE expert layer on one MI355X.
 
 A step is one pass of the whole layer path (route -> align -> expert FFN with
-combine) over every layer of the workload, on one stream (captured as a HIP
+combine) over every layer of a workload, on one stream (captured as a HIP
 graph unless --eager). Inputs are synthetic (gen/) and resident in HBM before
 the timed region. Prints one JSON line.
 
-Default workload: the decode-regime layer stack -- T=32 tokens through 40
-layers of H=2048, I=512, E=256, top-8, each with its own 102-slot FP8 pool
-(grown to hold every routed expert when more are needed).
+Default run: the headline workload is the decode-regime layer stack, T=32
+tokens through 40 layers of H=2048, I=512, E=256, top-8, each with its own
+102-slot FP8 pool (grown to hold every routed expert when more are needed).
+The same line carries one record per other workload ("records"): the other
+decode stacks (T=8; the larger-expert stack at T=32; the mixed FP8/int4
+stack at T=8) and the batched layers (16384 accumulated tokens; 4096 tokens
+of the larger-expert stack; 8192 tokens of the mixed stack). Each record has
+its layer time, layer-level HBM and FP8-matrix fractions, the roofline of
+its dominant kernel and the oracle's CPU baseline. The roofline is the FP8
+matrix peak for the 16384-token layer (a dense contraction) and HBM
+bandwidth for every other workload.
 """
 import argparse
 import hashlib
@@ -24,7 +32,10 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
-BF16_PEAK_TFLOPS = 2500.0
+
+# (config, tokens): the headline first, then the other records of the default run
+DEFAULT_RUN = [("C1", 32), ("C1", 8), ("C3", 32), ("C4", 8), ("C2", 16384), ("C3", 4096), ("C4", 8192)]
+MFMA_BOUND = {("C2", 16384)}          # dense contraction: FP8 matrix roofline; everything else: HBM
 
 
 def parse():
@@ -32,8 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="C1")
-    ap.add_argument("--tokens", type=int, default=None, help="tokens per layer (default: largest decode T)")
+    ap.add_argument("--config", default=None, help="measure one workload only (default: every workload)")
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per layer (with --config)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--act", choices=["auto", "bf16", "fp8"], default="auto")
@@ -41,7 +52,8 @@ def parse():
     ap.add_argument("--calls", choices=("layer", "split"), default="layer",
                     help="layer: one moe_layer call per layer; split: moe_route_align then moe_expert_ffn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget of the headline workload")
+    ap.add_argument("--cpu-seconds-records", type=float, default=5.0, help="... of each other record")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
@@ -59,29 +71,34 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the layer runs unsharded on one MI355X); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
+def host_info():
+    """CPU model and BLAS build of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')} ({b.get('openblas configuration', '').strip()})"
+    except Exception:
+        pass
+    return model, blas
+
+
+def measure(args, name, T, L, cpu_seconds, mfma_bound):
     import torch
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}))
-        return
     import moe_expert_layer_topk_amd as moe
     from gen import CONFIGS, make_layer, make_bank
     from harness import device_pool, device_inputs, bank_on_device, oracle_layer
 
-    cfg = CONFIGS[args.config]
-    T = args.tokens or (max(t for t in cfg.Ts if t <= 64) if min(cfg.Ts) <= 64 else cfg.Ts[0])
-    L = args.layers or cfg.layers
+    cfg = CONFIGS[name]
     act = {"bf16": moe.ACT_BF16, "fp8": moe.ACT_FP8_G128_POW2}.get(args.act)
     if act is None:
         act = moe.ACT_BF16 if T <= 64 else moe.ACT_FP8_G128_POW2
@@ -109,9 +126,9 @@ def main():
                    aws=torch.empty(max(1, moe.route_align_workspace_bytes(T, k, E, bm)), dtype=torch.uint8,
                                    device=dev),
                    fws=torch.empty(max(1, moe.ffn_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
-                                   device=dev),
+                                   device=dev) if args.calls == "split" else None,
                    lws=torch.empty(max(1, moe.layer_workspace_bytes(T, k, E, H, I, bm, act)), dtype=torch.uint8,
-                                   device=dev),
+                                   device=dev) if args.calls == "layer" else None,
                    out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
         layers.append((li, pool, x, logits, soe, mask, buf))
     del bdev
@@ -164,7 +181,8 @@ def main():
     tok_s = T * L / (ms_step / 1e3)          # expert-layer tokens per second
     log(f"[bench] {ms_step:.4f} ms/step, {ms_step / L * 1e3:.2f} us/layer (wall {wall:.3f}s)")
 
-    # ---- per-kernel durations with the library's event tracing, same steps eagerly
+    # ---- per-kernel durations with the library's event tracing (HIP events
+    # the dispatches stamp on the launch stream), same steps launched eagerly
     moe.profile_enable(True)
     for _ in range(args.steps):
         step()
@@ -173,50 +191,73 @@ def main():
     moe.profile_enable(False)
     log("[bench] kernels: " + ", ".join(f"{n}: {c} x {ms / c * 1e3:.2f} us" for n, (c, ms) in prof.items()))
 
-    # ---- algorithmic work per layer
-    slot_used = {0: moe.slot_bytes(H, I, 0), 1: moe.slot_bytes(H, I, 1) if I % 128 == 0 else 0}
+    # ---- algorithmic work per layer (distinct routed experts' slot bytes, not padding)
     w13_bytes = {0: 2 * I * H + 8 * I, 1: I * H + 2 * I * (H // 128) * 4}
     w2_bytes = {0: H * I + 4 * H, 1: H * I // 2 + H * (I // 128) * 4}
-    tot_bytes = tot_flops = g1_bytes = g2_bytes = 0
-    distinct = []
+    NP = T * k
+    tot_bytes = tot_flops = 0
+    kern_bytes = {}          # per kernel, summed over layers
+    kern_flops = {}
+    distinct, fmt_hist = [], {"fp8": 0, "int4": 0}
     for li, pool, x, logits, soe, mask, b in layers:
         ids = b["ids"].cpu().numpy()
-        used = np.unique(ids[ids >= 0])
+        used, cnt = np.unique(ids[ids >= 0], return_counts=True)
         distinct.append(used.size)
-        fm = li.expert_fmt[used]
-        w13 = sum(w13_bytes[int(f)] for f in fm)
-        w2 = sum(w2_bytes[int(f)] for f in fm)
-        NP = T * k
+        fm = li.expert_fmt[used].astype(int)
+        fmt_hist["fp8"] += int((fm == 0).sum())
+        fmt_hist["int4"] += int((fm == 1).sum())
+        w13 = sum(w13_bytes[f] for f in fm)
+        w2 = sum(w2_bytes[f] for f in fm)
+        w13_fp8 = sum(w13_bytes[0] for f in fm if f == 0)
+        w2_fp8 = sum(w2_bytes[0] for f in fm if f == 0)
+        np_fp8 = int(cnt[fm == 0].sum())
         tot_bytes += w13 + w2 + T * H * 2 + T * E * 4 + T * H * 2 + NP * 16
         tot_flops += 6 * NP * H * I
-        g1_bytes += w13 + T * H * 2 + NP * I * 2
-        g2_bytes += w2 + NP * I * 2 + T * H * 2
+
+        def add(d, key, v):
+            d[key] = d.get(key, 0) + v
+        # decode kernels: weights of every routed expert + token rows + h rows
+        add(kern_bytes, "gemm1_stream", w13 + T * H * 2 + NP * I * 2)
+        add(kern_bytes, "gemm2_stream", w2 + NP * I * 2 + NP * H * 4)
+        # batched FP8 matrix-core kernels: FP8-slot experts' weights, activation codes, h codes
+        add(kern_bytes, "gemm1_fp8", w13_fp8 + T * H + np_fp8 * I)
+        add(kern_bytes, "gemm2_fp8", w2_fp8 + np_fp8 * I + np_fp8 * H * 2)
+        add(kern_bytes, "gemm1_tile", (w13 - w13_fp8) + (NP - np_fp8) * (H + I))
+        add(kern_bytes, "gemm2_tile", (w2 - w2_fp8) + (NP - np_fp8) * (I + H * 2))
+        add(kern_bytes, "combine", NP * H * (4 if act == moe.ACT_BF16 else 2) + T * H * 2)
+        add(kern_flops, "gemm1_fp8", 4 * np_fp8 * H * I)
+        add(kern_flops, "gemm2_fp8", 2 * np_fp8 * H * I)
     layer_s = ms_step / 1e3 / L
     hbm_frac_layer = tot_bytes / L / layer_s / (HBM_PEAK_GBS * 1e9)
-    if act == moe.ACT_BF16:
-        dom = "gemm1_stream"
-        n, ms = prof[dom]
-        achieved = (g1_bytes / L) / (ms / n / 1e3) / 1e9        # bytes of one launch / its mean duration
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4))
-        dtype = "bf16"
-    else:
-        dom = "gemm1_fp8"
-        n, ms = prof[dom]
-        flops = 4 * T * k * H * I                               # gate + up contraction of one launch
-        achieved = flops / (ms / n / 1e3) / 1e12
+    mfma_frac_layer = tot_flops / L / layer_s / (FP8_PEAK_TFLOPS * 1e12)
+
+    # dominant kernel: the one with the most time per step
+    dom = max(prof, key=lambda n: prof[n][1])
+    n_launch, ms = prof[dom]
+    per_launch_s = ms / n_launch / 1e3
+    launches_per_step = n_launch / args.steps
+    if mfma_bound:
+        work = kern_flops.get(dom, 0) / launches_per_step
+        achieved = work / per_launch_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / FP8_PEAK_TFLOPS, 4))
-        dtype = "fp8"
+    else:
+        work = kern_bytes.get(dom, 0) / launches_per_step
+        achieved = work / per_launch_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
     roof["kernel"] = dom
-    roof["avg_us"] = round(ms / n * 1e3, 3)
+    roof["avg_us"] = round(per_launch_s * 1e6, 3)
+    roof["work_per_launch"] = int(work)
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         rec = json.load(open(tpath)).get(f"{cfg.name}-T{T}-{dom}")
-        if rec and rec.get("source_hash") == source_hash("ffn_stream.hip" if act == moe.ACT_BF16 else "ffn_mfma.hip"):
+        srcs = ("ffn_stream.hip",) if act == moe.ACT_BF16 else ("ffn_mfma.hip", "ffn_grouped.hip")
+        if rec and rec.get("source_hash") == source_hash(*srcs):
             traffic = rec.get("bytes_per_launch")
     roof["traffic"] = traffic
+    roof["layer_frac"] = round(mfma_frac_layer if mfma_bound else hbm_frac_layer, 4)
 
     # ---- CPU baseline: the oracle on a bounded sample of the same layers
     cpu = None
@@ -232,7 +273,7 @@ def main():
                 t_cpu += time.perf_counter() - c0
                 done_tok += T
                 n_layers += 1
-                if t_cpu >= args.cpu_seconds:
+                if t_cpu >= cpu_seconds:
                     break
             what = f"{n_layers} of {L} layers, all {T} tokens each"
         else:
@@ -246,30 +287,75 @@ def main():
                 c0 = time.perf_counter()
                 oracle_layer(li, bank, bm, act, token_subset=sub)
                 t_cpu = time.perf_counter() - c0
-                if t_cpu >= args.cpu_seconds / 3 or n >= T:
+                if t_cpu >= cpu_seconds / 3 or n >= T:
                     break
                 n *= 4
             done_tok = sub.size
             what = f"layer 0, FFN of {sub.size} of {T} tokens (route and align on all {T})"
+        model, blas = host_info()
         cpu = dict(value=round(done_tok / t_cpu, 3), unit="tokens/s", cores=threads, kind="oracle",
-                   sample=f"{what}; fp64 NumPy incl. slot dequant; {t_cpu:.1f}s")
+                   sample=f"{what}; fp64 NumPy incl. slot dequant; {t_cpu:.1f}s", cpu_model=model, blas=blas)
         log(f"[bench] cpu oracle {cpu['value']} tokens/s over {t_cpu:.1f}s")
 
+    rec = dict(
+        workload=f"{cfg.name}: T={T} tokens x {L} layers, H={H}, I={I}, E={E}, top-{k}, "
+                 f"{'per-layer slot pools' if cfg.slots and T < cfg.resident_all_at else 'all experts resident'}, "
+                 f"{'FP8 + int4' if cfg.int4_frac else 'FP8'} slots",
+        value=round(tok_s, 1), ms_per_step=round(ms_step, 5), tokens_per_layer=T, layers=L, block_m=bm,
+        act_mode="bf16" if act == moe.ACT_BF16 else "fp8_g128_pow2", graph=graph is not None,
+        distinct_experts_per_layer=round(float(np.mean(distinct)), 1),
+        slot_formats_routed=fmt_hist,
+        layer_us=round(layer_s * 1e6, 3), layer_hbm_frac=round(hbm_frac_layer, 4),
+        layer_mfma_frac=round(mfma_frac_layer, 4), layer_tflops=round(tot_flops / L / layer_s / 1e12, 2),
+        kernels_us={n: round(m / c * 1e3, 3) for n, (c, m) in prof.items()},
+        roofline=roof, cpu_baseline=cpu, dtype="bf16" if act == moe.ACT_BF16 else "fp8")
+    # free this workload's device memory before the next one
+    del layers, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer runs unsharded on one MI355X); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}))
+        return
+    from gen import CONFIGS
+
+    if args.config:
+        cfg = CONFIGS[args.config]
+        T = args.tokens or (max(t for t in cfg.Ts if t <= 64) if min(cfg.Ts) <= 64 else cfg.Ts[0])
+        runs = [(args.config, T)]
+    else:
+        runs = DEFAULT_RUN
+    recs = []
+    for i, (name, T) in enumerate(runs):
+        L = args.layers or CONFIGS[name].layers
+        recs.append(measure(args, name, T, L, args.cpu_seconds if i == 0 else args.cpu_seconds_records,
+                            (name, T) in MFMA_BOUND))
+    head = recs[0]
     res = {
         "metric": "MoE expert-layer tokens/s (layer tokens per second over the layer stack)",
-        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": dtype, "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: T={T} tokens x {L} layers, H={H}, I={I}, E={E}, top-{k}, "
-                               f"{'per-layer slot pools' if cfg.slots else 'all experts resident'}, "
-                               f"{'FP8 + int4' if cfg.int4_frac else 'FP8'} slots",
-                   "tokens_per_layer": T, "layers": L, "block_m": bm,
-                   "act_mode": "bf16" if act == moe.ACT_BF16 else "fp8_g128_pow2",
-                   "graph": graph is not None, "distinct_experts_per_layer": round(float(np.mean(distinct)), 1),
-                   "layer_us": round(layer_s * 1e6, 3), "layer_hbm_frac": round(hbm_frac_layer, 4),
-                   "layer_tflops": round(tot_flops / L / layer_s / 1e12, 2)},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic",
+        "config": {k: v for k, v in head.items() if k not in ("value", "ms_per_step", "roofline", "cpu_baseline",
+                                                              "dtype")},
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "records": recs[1:],
     }
     print(json.dumps(res), flush=True)
 

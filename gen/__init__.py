@@ -12,3 +12,4 @@ from .inputs import (  # noqa: F401
     ExpertBank, LayerInputs, make_layer, make_bank, bf16_round, bf16_bits_to_f64,
     layer_pool_bytes, zipf_prior, encode_slot, INT4_GROUP,
 )
+from .exact import make_integer_layer, integer_weights, IntegerBank  # noqa: F401

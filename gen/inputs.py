@@ -60,10 +60,13 @@ def slot_layout(H: int, I: int, fmt: int) -> Dict[str, tuple]:
                  ("w2", H * I // 2), ("w2_sz", H * (I // INT4_GROUP) * 4)]
     else:
         raise ValueError(f"unknown slot format {fmt}")
+    # an int4 slot keeps 16 spare bytes after its last array (the library's
+    # layout: its kernels read (scale, zero) rows 16 bytes at a time)
+    tail = 16 if fmt == FMT_INT4_G128 else 0
     out, off = {}, 0
-    for name, n in parts:
+    for i, (name, n) in enumerate(parts):
         out[name] = (off, n)
-        off = _al(off + n)
+        off = _al(off + n + (tail if i == len(parts) - 1 else 0))
     out["total"] = (0, off)
     return out
 

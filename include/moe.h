@@ -122,13 +122,16 @@ int moe_route_align(const float* d_logits, const uint8_t* d_mask, int T, int E, 
  *               INT4 W[r][c] = (q[r][c] - zero[r][c/128]) * scale[r][c/128].
  *  INT4 zero points are integers in [0, 15] (stored as fp16): the kernels
  *  form q - zero exactly as a small integer before the matrix instructions
- *  and apply the group scale after them.
+ *  and apply the group scale after them (moe_pool_check finds other zeros).
+ *  An INT4 slot keeps 16 spare bytes after w2_sz before its size is rounded
+ *  up to 256 (moe_slot_bytes includes them).
  * Rows [0, I) of w13 are the gate projection, rows [I, 2I) the up projection.
  * d_slot_fmt is a device array u8[n_slots] of MOE_FMT_* values.
  * hidden % 128 == 0, inter % 64 == 0 (INT4 slots: inter % 128 == 0). */
 typedef struct moe_slot_pool {
     void*          d_base;
-    size_t         slot_bytes;   /* >= moe_slot_bytes of every format used, multiple of 256 */
+    size_t         slot_bytes;   /* multiple of 256, >= moe_slot_bytes of some format; slots
+                                    whose format does not fit are unusable (not resident) */
     int            n_slots;
     const uint8_t* d_slot_fmt;
     int            hidden;
@@ -143,7 +146,9 @@ size_t moe_slot_part_offset(int hidden, int inter, int fmt, int part);
  * [VEP] Table 1 set-up and "hierarchical paging" section: the expert's w13
  * and w2 are read from its slot; [PW] "what was released": the layer output
  * mixes the chosen experts' outputs. For every pair p = t*k + j listed in
- * block b (slot s = block_slot[b], skipped if s < 0):
+ * block b (slot s = block_slot[b]; skipped, adding zero, when s is not
+ * usable: negative, >= n_slots, or tagged with a format that is not FP8 or
+ * int4 or does not fit slot_bytes):
  *    gu = W13[s] a_t, h = silu(gu[0:I]) * gu[I:2I], y = W2[s] h,
  *    out[t] = sum_j topk_w[t][j] * y_(t,j), accumulated in fp32, then bf16.
  * a_t is token row t of x in the precision act_mode selects.
@@ -170,7 +175,10 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
  * hidden <= 2048) take fewer launches: every workgroup of the gate/up kernel
  * sorts the pairs in its own LDS instead of waiting for an align launch, and
  * for T <= 16 also routes the tokens itself; other shapes run the separate
- * calls' kernels. The workspace holds moe_layer_workspace_bytes bytes (0 =
+ * calls' kernels. The slot table is checked against the pool: an entry that
+ * is not usable (>= n_slots, or a slot whose tag is not a usable format)
+ * counts like -1 (d_block_slot gets -1, its pairs add zero and count in
+ * d_err[1]). The workspace holds moe_layer_workspace_bytes bytes (0 =
  * invalid arguments). Errors: MOE_EINVAL for the arguments any of the three
  * calls rejects. */
 size_t moe_layer_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode);
@@ -180,10 +188,48 @@ int moe_layer(const moe_slot_pool* pool, const float* d_logits, const uint8_t* d
               int32_t* d_counts, int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err,
               uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- activation quantize
+ * The activation step of MOE_ACT_FP8_G128_POW2 on its own (the FP8 matrix
+ * cores of the grouped contraction need FP8 operands; MOE-GEN explainer,
+ * aibr.jp, section 3: per-expert batches are dense contractions). For every
+ * row r and group g of 128 consecutive columns: s = the smallest integer with
+ * max|x[r][128g..128g+127]| <= 448 * 2^s (s = 0 for an all-zero group),
+ * clamped to [-127, 127]; d_codes[r][c] = e4m3 code of x[r][c] / 2^s,
+ * rounded to nearest even (x / 2^s is exact); d_exps[r][g] = s + 127 (the
+ * E8M0 byte the scaled matrix instruction takes).
+ *  d_x bf16 [rows, cols]; d_codes u8 [rows, cols]; d_exps u8 [rows, cols/128].
+ * cols must be a positive multiple of 128. */
+int moe_quant_act(const uint16_t* d_x, int rows, int cols, uint8_t* d_codes, uint8_t* d_exps, void* stream);
+
+/* ---------------------------------------------------------------- pool check
+ * [VEP] "hierarchical paging of expert weights": slots are refilled while
+ * the model runs. Every FFN call treats a slot as not resident (its pairs add
+ * zero) when its index is outside [0, n_slots), its tag is neither format, or
+ * its format's layout does not fit slot_bytes; moe_layer also counts such
+ * pairs in d_err[1] and writes -1 for their blocks in d_block_slot.
+ * moe_pool_check reports, for every slot, whether it is usable and why not:
+ * d_status u8 [n_slots] (may be NULL): 0 usable, 1 the tag is not a format,
+ * 2 the format does not fit the stride, 3 an int4 group whose zero point is
+ * not an integer in [0, 15] or whose scale is not finite (the kernels form
+ * q - zero exactly only for such zero points), 4 an FP8 row scale that is
+ * not finite. d_err i32 [1] gets +1 per slot with a nonzero status. */
+int moe_pool_check(const moe_slot_pool* pool, int32_t* d_err, uint8_t* d_status, void* stream);
+
+/* ---------------------------------------------------------------- debug
+ * moe_debug_poison(1): every later FFN call (moe_expert_ffn, moe_layer)
+ * first fills the data regions of its workspace (activation codes, h rows,
+ * weighted pair rows) with all-ones bytes, NaN in every float format used,
+ * so a read of workspace data the call did not write first shows up as NaN
+ * in d_out. Outputs are unchanged when nothing reads unwritten data. A
+ * debugging aid (one extra fill per call); moe_debug_poison(0) turns it off.
+ * Process-wide. */
+int moe_debug_poison(int on);
+
 /* ---------------------------------------------------------------- dequant
  * [PW] "technically interesting points": per-expert bit width. Writes the
  * dequantized matrices of slot `slot` in fp32: d_w13 [2I][H], d_w2 [H][I]
- * (either may be NULL). */
+ * (either may be NULL). An unusable slot (see moe_pool_check, statuses 1
+ * and 2) yields NaN matrices. */
 int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream);
 
 /* ---------------------------------------------------------------- tracing

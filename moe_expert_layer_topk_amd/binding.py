@@ -52,6 +52,9 @@ def _declare(lib):
         "moe_layer": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, c_int, c_int, c_int, c_int, c_int, P,
                               P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "moe_dequant_slot": (c_int, [ctypes.POINTER(moe_slot_pool), c_int, P, P, P]),
+        "moe_quant_act": (c_int, [P, c_int, c_int, P, P, P]),
+        "moe_pool_check": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P]),
+        "moe_debug_poison": (c_int, [c_int]),
         "moe_profile_enable": (c_int, [c_int]),
         "moe_profile_kernels": (c_int, []),
         "moe_profile_kernel_name": (ctypes.c_char_p, [c_int]),
@@ -272,6 +275,32 @@ def dequant_slot(pool, slot, w13=None, w2=None, stream=None):
     _check(lib().moe_dequant_slot(pool.c_ref(), slot, _ptr(w13, torch.float32, 2 * I * H, "w13"),
                                   _ptr(w2, torch.float32, H * I, "w2"), _stream(stream)))
     return w13, w2
+
+
+def quant_act(x, codes=None, exps=None, stream=None):
+    """moe_quant_act: e4m3 codes uint8 [rows, cols] and E8M0 bytes uint8 [rows, cols / 128]."""
+    import torch
+    R, C = x.shape
+    codes = torch.empty((R, C), dtype=torch.uint8, device=x.device) if codes is None else codes
+    exps = torch.empty((R, C // 128), dtype=torch.uint8, device=x.device) if exps is None else exps
+    _check(lib().moe_quant_act(_ptr(x, torch.bfloat16, R * C, "x"), R, C, _ptr(codes, torch.uint8, R * C, "codes"),
+                               _ptr(exps, torch.uint8, R * (C // 128), "exps"), _stream(stream)))
+    return codes, exps
+
+
+def pool_check(pool, err=None, status=None, stream=None):
+    """moe_pool_check: (err i32[1], status u8[n_slots]) on the device."""
+    import torch
+    dev = pool.data.device
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    status = torch.empty(pool.n_slots, dtype=torch.uint8, device=dev) if status is None else status
+    _check(lib().moe_pool_check(pool.c_ref(), _ptr(err, torch.int32, 1, "err"),
+                                _ptr(status, torch.uint8, pool.n_slots, "status"), _stream(stream)))
+    return err, status
+
+
+def debug_poison(on=True):
+    _check(lib().moe_debug_poison(1 if on else 0))
 
 
 # ---------------------------------------------------------------- tracing

@@ -39,10 +39,14 @@ void slot_parts(int H, int I, int fmt, size_t off[4], size_t* total) {
         sz[2] = (size_t)H * I / 2;
         sz[3] = (size_t)H * (I / 128) * 4;
     }
+    // An int4 slot keeps 16 bytes after its last array: the kernels read a
+    // row's (scale, zero) pairs 16 bytes at a time, which for rows of fewer
+    // than four groups runs up to 12 bytes past the row.
+    const size_t tail = fmt == MOE_FMT_INT4_G128 ? 16 : 0;
     size_t o = 0;
     for (int i = 0; i < 4; ++i) {
         off[i] = o;
-        o = up256(o + sz[i]);
+        o = up256(o + sz[i] + (i == 3 ? tail : 0));
     }
     if (total) *total = o;
 }
@@ -51,6 +55,7 @@ bool pool_args(const moe_slot_pool* pool, moe::PoolArgs* pa) {
     if (!pool || !pool->d_base || !pool->d_slot_fmt || pool->n_slots < 1 || pool->n_slots > MOE_MAX_SLOTS) return false;
     const int H = pool->hidden, I = pool->inter;
     if (H < 128 || H % 128 || I < 64 || I % 64) return false;
+    if (pool->slot_bytes % 256) return false;
     size_t fp8_bytes, int4_bytes = 0;
     slot_parts(H, I, MOE_FMT_FP8_E4M3_ROW, pa->off[0], &fp8_bytes);
     if (I % 128 == 0) {
@@ -58,10 +63,12 @@ bool pool_args(const moe_slot_pool* pool, moe::PoolArgs* pa) {
     } else {
         for (int i = 0; i < 4; ++i) pa->off[1][i] = pa->off[0][i];   // int4 slots need inter % 128 == 0
     }
-    // The formats live on the device; the stride must at least hold the
-    // smallest format (the caller guarantees it holds every format it uses).
-    const size_t smallest = int4_bytes ? int4_bytes : fp8_bytes;
-    if (pool->slot_bytes % 256 || pool->slot_bytes < smallest) return false;
+    // The tags live on the device; a format whose layout does not fit the
+    // stride makes the slots tagged with it unusable (treated as not
+    // resident), and a stride that fits neither format is refused.
+    pa->fmt_ok = (pool->slot_bytes >= fp8_bytes ? 1 : 0) | (int4_bytes && pool->slot_bytes >= int4_bytes ? 2 : 0);
+    if (!pa->fmt_ok) return false;
+    pa->spec_fmt = (pa->fmt_ok & 1) ? MOE_FMT_FP8_E4M3_ROW : MOE_FMT_INT4_G128;
     pa->base = pool->d_base;
     pa->stride = pool->slot_bytes;
     pa->fmt = pool->d_slot_fmt;
@@ -236,15 +243,41 @@ int moe_layer(const moe_slot_pool* pool, const float* d_logits, const uint8_t* d
                                                    d_n_padded, d_err, cap, d_out, (uint8_t*)d_ws + aws,
                                                    (hipStream_t)stream));
     }
-    // other shapes: the separate calls, on the same stream
+    // other shapes: the separate calls' kernels, on the same stream; the
+    // align step checks the slot table against the pool
     const size_t aws_bytes = moe_route_align_workspace_bytes(T, k, E, block_m);
     const size_t aws = up256(aws_bytes);
-    int st = moe_route_align(d_logits, d_mask, T, E, k, block_m, d_slot_of_expert, d_topk_ids, d_topk_w,
-                             d_sorted_pair, d_block_slot, d_counts, d_seg_offset, d_n_padded, d_err,
-                             aws_bytes ? d_ws : nullptr, aws_bytes, stream);
+    moe::SlotCheck chk;
+    chk.fmt = pa.fmt;
+    chk.n_slots = pa.n_slots;
+    chk.fmt_ok = pa.fmt_ok;
+    clear_stale_error();
+    int st = hip_status(moe::launch_route_align(d_logits, d_mask, T, E, k, block_m, d_slot_of_expert, d_topk_ids,
+                                                d_topk_w, d_sorted_pair, d_block_slot, d_counts, d_seg_offset,
+                                                d_n_padded, d_err, aws_bytes ? d_ws : nullptr, (hipStream_t)stream,
+                                                chk));
     if (st != MOE_OK) return st;
     return moe_expert_ffn(pool, d_x, T, k, E, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded, block_m, act_mode,
                           d_out, (uint8_t*)d_ws + aws, ws_bytes - aws, stream);
+}
+
+int moe_quant_act(const uint16_t* d_x, int rows, int cols, uint8_t* d_codes, uint8_t* d_exps, void* stream) {
+    if (!d_x || !d_codes || !d_exps || rows < 1 || cols < MOE_ACT_G || cols % MOE_ACT_G) return MOE_EINVAL;
+    if ((long long)rows * (cols / MOE_ACT_G) >= (1LL << 31)) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_quant_act(d_x, rows, cols, d_codes, d_exps, (hipStream_t)stream));
+}
+
+int moe_pool_check(const moe_slot_pool* pool, int32_t* d_err, uint8_t* d_status, void* stream) {
+    moe::PoolArgs pa;
+    if (!pool_args(pool, &pa) || !d_err) return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_pool_check(pa, d_err, d_status, (hipStream_t)stream));
+}
+
+int moe_debug_poison(int on) {
+    moe::set_debug_poison(on);
+    return MOE_OK;
 }
 
 int moe_dequant_slot(const moe_slot_pool* pool, int slot, float* d_w13, float* d_w2, void* stream) {

@@ -59,20 +59,26 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
 
 // From per-expert counts: padded offsets, n_padded, block -> slot map, the
 // sentinel padding of every segment tail, and the non-resident pair count.
-// One block of ALIGN_THREADS threads; counts in s_cnt[E].
-__device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_tmp, int E, int block_m, int sentinel,
-                                     const int32_t* slot_of_expert, int32_t* counts, int32_t* seg_offset,
-                                     int32_t* n_padded, int32_t* block_slot, int32_t* sorted_pair, int32_t* err) {
+// One block of ALIGN_THREADS threads; counts in s_cnt[E]. With a slot check,
+// an entry outside the pool or with an unusable format counts as -1 (not
+// resident).
+__device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_sl, int* s_tmp, int E, int block_m,
+                                     int sentinel, const int32_t* slot_of_expert, SlotCheck chk, int32_t* counts,
+                                     int32_t* seg_offset, int32_t* n_padded, int32_t* block_slot,
+                                     int32_t* sorted_pair, int32_t* err) {
     const int e = threadIdx.x;
     int c = e < E ? s_cnt[e] : 0;
+    int sl = e < E ? slot_of_expert[e] : -1;
+    if (chk.fmt && sl >= 0) sl = usable_slot(sl, chk.n_slots, chk.fmt_ok, chk.fmt);
     int padded = (c + block_m - 1) / block_m * block_m;
     int total;
     int off = block_exclusive_scan(padded, s_tmp, total);
     if (e < E) {
         s_off[e] = off;
+        s_sl[e] = sl;
         counts[e] = c;
         seg_offset[e] = off;
-        if (slot_of_expert[e] < 0 && c > 0) atomicAdd(err, c);
+        if (sl < 0 && c > 0) atomicAdd(err, c);
     }
     if (e == 0) {
         seg_offset[E] = total;
@@ -92,7 +98,7 @@ __device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_tmp, i
             if (s_off[mid] <= pos) lo = mid;
             else hi = mid - 1;
         }
-        block_slot[b] = slot_of_expert[lo];
+        block_slot[b] = s_sl[lo];
         for (int q = max(pos, s_off[lo] + s_cnt[lo]); q < pos + block_m; ++q) sorted_pair[q] = sentinel;
     }
     __syncthreads();
@@ -135,9 +141,10 @@ __device__ void scatter_pairs(const int32_t* ids, int p0, int p1, int E, int* s_
 __global__ void __launch_bounds__(ALIGN_THREADS) align_single_kernel(
     const int32_t* __restrict__ ids, int NP, int E, int block_m, const int32_t* __restrict__ slot_of_expert,
     int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
-    int32_t* err) {
+    int32_t* err, SlotCheck chk) {
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_run[MOE_MAX_E];
+    __shared__ int s_sl[MOE_MAX_E];
     __shared__ int s_tmp[2 * ALIGN_WAVES];
     __shared__ uint8_t s_wcnt[ALIGN_WAVES * MOE_MAX_E];
     for (int i = threadIdx.x; i < E; i += ALIGN_THREADS) s_cnt[i] = 0;
@@ -150,8 +157,8 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_single_kernel(
     }
     if (bad) atomicAdd(err, bad);
     __syncthreads();
-    segments_from_counts(s_cnt, s_run, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
-                         block_slot, sorted_pair, err);
+    segments_from_counts(s_cnt, s_run, s_sl, s_tmp, E, block_m, NP, slot_of_expert, chk, counts, seg_offset,
+                         n_padded, block_slot, sorted_pair, err);
     scatter_pairs(ids, 0, NP, E, s_run, s_wcnt, sorted_pair);
 }
 
@@ -177,9 +184,10 @@ __global__ void __launch_bounds__(256) align_hist_kernel(const int32_t* __restri
 __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
     int32_t* __restrict__ hist, int n_chunks, int NP, int E, int block_m,
     const int32_t* __restrict__ slot_of_expert, int32_t* sorted_pair, int32_t* block_slot, int32_t* counts,
-    int32_t* seg_offset, int32_t* n_padded, int32_t* err) {
+    int32_t* seg_offset, int32_t* n_padded, int32_t* err, SlotCheck chk) {
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_off[MOE_MAX_E];
+    __shared__ int s_sl[MOE_MAX_E];
     __shared__ int s_tmp[2 * ALIGN_WAVES];
     const int e = threadIdx.x;
     constexpr int B = 32;                // chunk counts loaded per round trip (clamped, no branches)
@@ -200,8 +208,8 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_scan_kernel(
         s_cnt[e] = c;
     }
     __syncthreads();
-    segments_from_counts(s_cnt, s_off, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
-                         block_slot, sorted_pair, err);
+    segments_from_counts(s_cnt, s_off, s_sl, s_tmp, E, block_m, NP, slot_of_expert, chk, counts, seg_offset,
+                         n_padded, block_slot, sorted_pair, err);
     if (e < E) {                         // hist[b][e] <- start of chunk b's pairs of expert e
         int run = s_off[e];
         for (int b0 = 0; b0 < n_chunks; b0 += B) {
@@ -235,10 +243,11 @@ constexpr int MASK_MAX_T = 64;
 __global__ void __launch_bounds__(ALIGN_THREADS) align_mask_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int block_m, const int32_t* __restrict__ slot_of_expert,
     int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
-    int32_t* err) {
+    int32_t* err, SlotCheck chk) {
     __shared__ unsigned long long s_tok[MOE_MAX_E];   // bit t set: token t chose the expert
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_off[MOE_MAX_E];
+    __shared__ int s_sl[MOE_MAX_E];
     __shared__ int s_tmp[2 * ALIGN_WAVES];
     __shared__ uint8_t s_wcnt[ALIGN_WAVES * MOE_MAX_E];
     const int tid = threadIdx.x;
@@ -259,8 +268,8 @@ __global__ void __launch_bounds__(ALIGN_THREADS) align_mask_kernel(
     __syncthreads();
     // a token listing one expert twice breaks the mask ranks: take the counting path then
     const bool dup = __syncthreads_or(tid < E && s_cnt[tid] != (int)__popcll(s_tok[tid]));
-    segments_from_counts(s_cnt, s_off, s_tmp, E, block_m, NP, slot_of_expert, counts, seg_offset, n_padded,
-                         block_slot, sorted_pair, err);
+    segments_from_counts(s_cnt, s_off, s_sl, s_tmp, E, block_m, NP, slot_of_expert, chk, counts, seg_offset,
+                         n_padded, block_slot, sorted_pair, err);
     if (dup) {
         scatter_pairs(ids, 0, NP, E, s_off, s_wcnt, sorted_pair);
         return;
@@ -277,12 +286,12 @@ int route_align_fused_max_pairs() { return MASK_MAX_T; }
 hipError_t launch_route_align(const float* logits, const uint8_t* mask, int T, int E, int k, int block_m,
                               const int32_t* slot_of_expert, int32_t* ids, float* w, int32_t* sorted_pair,
                               int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
-                              int32_t* err, void* ws, hipStream_t stream) {
+                              int32_t* err, void* ws, hipStream_t stream, SlotCheck chk) {
     // the route error count lands in err[0]; align counts the -1 entries of short tokens in err[1]
     hipError_t e = launch_route(logits, mask, T, E, k, ids, w, err, stream);
     if (e != hipSuccess) return e;
     return launch_align(ids, T, k, E, block_m, slot_of_expert, sorted_pair, block_slot, counts, seg_offset,
-                        n_padded, err + 1, ws, stream);
+                        n_padded, err + 1, ws, stream, chk);
 }
 
 int align_single_max_pairs() { return 8192; }
@@ -295,23 +304,23 @@ size_t align_workspace_bytes(int NP, int E) {
 
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, const int32_t* slot_of_expert,
                         int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset,
-                        int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream) {
+                        int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream, SlotCheck chk) {
     const int NP = T * k;
     if (T <= MASK_MAX_T && NP <= ALIGN_THREADS) {
         MOE_LAUNCH(K_ALIGN_SINGLE, stream, align_mask_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, ids, T, k, E,
-                   block_m, slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+                   block_m, slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err, chk);
         return hipGetLastError();
     }
     if (NP <= align_single_max_pairs()) {
         MOE_LAUNCH(K_ALIGN_SINGLE, stream, align_single_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, ids, NP, E, block_m,
-                           slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+                           slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err, chk);
         return hipGetLastError();
     }
     int chunks = (NP + ALIGN_CHUNK - 1) / ALIGN_CHUNK;
     int32_t* hist = (int32_t*)ws;
     MOE_LAUNCH(K_ALIGN_HIST, stream, align_hist_kernel, dim3(chunks), dim3(256), 0, stream, ids, NP, E, hist, err);
     MOE_LAUNCH(K_ALIGN_SCAN, stream, align_scan_kernel, dim3(1), dim3(ALIGN_THREADS), 0, stream, hist, chunks, NP, E, block_m,
-                       slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err);
+                       slot_of_expert, sorted_pair, block_slot, counts, seg_offset, n_padded, err, chk);
     MOE_LAUNCH(K_ALIGN_SCATTER, stream, align_scatter_kernel, dim3(chunks), dim3(ALIGN_THREADS), 0, stream, ids, NP, E, hist,
                        sorted_pair);
     return hipGetLastError();

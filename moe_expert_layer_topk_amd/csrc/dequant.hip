@@ -3,7 +3,9 @@
 //   FP8 : W[r][c] = e4m3(q[r][c]) * scale[r]
 //   INT4: W[r][c] = (q[r][c] - zero[r][c/128]) * scale[r][c/128]
 // The slot's format is read on the device, so the launch carries the array
-// offsets of both formats.
+// offsets of both formats. A tag that is neither format, or names a format
+// whose layout does not fit the pool stride, yields NaN matrices (nothing is
+// read from the slot).
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -14,17 +16,20 @@ struct DqOffsets {
 };
 
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ slot_base, const uint8_t* __restrict__ fmtp,
-                                                     int slot, DqOffsets off, int rows, int cols,
+                                                     int slot, int fmt_ok, DqOffsets off, int rows, int cols,
                                                      float* __restrict__ out) {
-    // int4 slots need a K (cols) multiple of the group; any other tag reads as FP8
-    const int fmt = (fmtp[slot] == 1 && cols % MOE_INT4_G == 0 && rows % 2 == 0) ? 1 : 0;
+    const int tag = fmtp[slot];
+    const bool usable = fmt_usable(tag, fmt_ok);
+    const int fmt = usable ? tag : 0;
     const uint8_t* codes = slot_base + off.codes[fmt];
     const uint8_t* scale = slot_base + off.scale[fmt];
     const size_t n = (size_t)rows * cols;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
         const int r = (int)(i / cols), c = (int)(i % cols);
         float v;
-        if (fmt == 0) {
+        if (!usable) {
+            v = __builtin_nanf("");
+        } else if (fmt == 0) {
             v = e4m3_to_f32(codes[i]) * ((const float*)scale)[r];
         } else {
             const uint8_t b = codes[(size_t)r * (cols / 2) + c / 2];
@@ -41,11 +46,13 @@ hipError_t launch_dequant(const PoolArgs& pa, int slot, float* w13, float* w2, h
     const int H = pa.hidden, I = pa.inter;
     if (w13) {
         DqOffsets o = {{pa.off[0][0], pa.off[1][0]}, {pa.off[0][1], pa.off[1][1]}};
-        MOE_LAUNCH(K_DEQUANT, stream, dequant_kernel, dim3(512), dim3(256), 0, stream, base, pa.fmt, slot, o, 2 * I, H, w13);
+        MOE_LAUNCH(K_DEQUANT, stream, dequant_kernel, dim3(512), dim3(256), 0, stream, base, pa.fmt, slot, pa.fmt_ok, o, 2 * I,
+                   H, w13);
     }
     if (w2) {
         DqOffsets o = {{pa.off[0][2], pa.off[1][2]}, {pa.off[0][3], pa.off[1][3]}};
-        MOE_LAUNCH(K_DEQUANT, stream, dequant_kernel, dim3(512), dim3(256), 0, stream, base, pa.fmt, slot, o, H, I, w2);
+        MOE_LAUNCH(K_DEQUANT, stream, dequant_kernel, dim3(512), dim3(256), 0, stream, base, pa.fmt, slot, pa.fmt_ok, o, H, I,
+                   w2);
     }
     return hipGetLastError();
 }

@@ -33,6 +33,8 @@ struct GPool {
     size_t stride;
     const uint8_t* fmt;
     size_t off[2][4];
+    int n_slots;
+    int fmt_ok;           // bit f: format f fits the stride (usable_slot)
 };
 
 __device__ __forceinline__ float2 f16x2_at(const uint8_t* p) {
@@ -75,6 +77,13 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restri
         *(uint2*)(xq + off) = make_uint2(w[0], w[1]);
         if ((lane & 15) == 0) xs[(size_t)r * groups + g] = (uint8_t)(s + 127);
     }
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* exps, hipStream_t stream) {
+    const long items = (long)rows * (cols / MOE_ACT_G);   // 16 per workgroup
+    MOE_LAUNCH(K_QUANT_ACT, stream, quant_act_kernel, dim3((unsigned)((items + 15) / 16)), dim3(256), 0, stream, x,
+               rows, cols, codes, exps);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------ shared GEMM pieces
@@ -143,10 +152,11 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
     float* s_amax = (float*)(s_xs + ((BM * groups + 15) / 16) * 16);   // [4][BM]
 
     if (mt_idx >= *n_padded / BM) return;
-    const int slot = block_slot[mt_idx];
+    // an unusable slot (not resident, outside the pool, format larger than the stride) adds nothing
+    const int slot = usable_slot(block_slot[mt_idx], pool.n_slots, pool.fmt_ok, pool.fmt);
     if (slot < 0) return;
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int fmt_slot = (pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;   // int4 needs inter % 128 == 0
+    const int fmt_slot = pool.fmt[slot];
     if (int4_only && fmt_slot == 0) return;
     const int fmt = ONLY4 ? 1 : fmt_slot;             // (the int4-only instance has no FP8 path)
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
@@ -365,11 +375,11 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
     uint8_t* sA = smem;                               // [BM][LDS_ROW]
     uint8_t* sB = sA + BM * LDS_ROW;                  // [128][LDS_ROW]
     if (mt_idx >= *n_padded / BM) return;
-    const int slot = block_slot[mt_idx];
+    const int slot = usable_slot(block_slot[mt_idx], pool.n_slots, pool.fmt_ok, pool.fmt);
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int n0 = nt_idx * 128;
-    if (int4_only && slot >= 0 && (pool.fmt[slot] != 1 || I % MOE_INT4_G != 0)) return;   // FP8: elsewhere
-    if (slot < 0) {                                   // non-resident expert: its pairs add zero
+    if (int4_only && slot >= 0 && pool.fmt[slot] != 1) return;   // FP8: elsewhere
+    if (slot < 0) {                                   // unusable slot (e.g. not resident): its pairs add zero
         for (int i = threadIdx.x; i < BM * 16; i += GT) {
             int r = i >> 4, ch = i & 15;
             int p = sorted_pair[mt_idx * BM + r];
@@ -379,7 +389,7 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
     }
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
     // int4 needs inter % 128 == 0; the int4-only instance has no FP8 path
-    const int fmt = ONLY4 ? 1 : ((pool.fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0);
+    const int fmt = ONLY4 ? 1 : (int)pool.fmt[slot];
     const int hgroups = (I + MOE_ACT_G - 1) / MOE_ACT_G;
     const int wgroups = I / MOE_INT4_G;
     f32x4 acc[MT][2];
@@ -632,7 +642,13 @@ hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int 
     gp.fmt = pa.fmt;
     for (int f = 0; f < 2; ++f)
         for (int p = 0; p < 4; ++p) gp.off[f][p] = pa.off[f][p];
+    gp.n_slots = pa.n_slots;
+    gp.fmt_ok = pa.fmt_ok;
     GroupedWs w = grouped_ws_layout(ws, T, k, pa.hidden, pa.inter, cap);
+    if (debug_poison_on()) {                          // activation codes, h and y rows: NaN until written
+        hipError_t e = launch_poison(ws, (size_t)((uint8_t*)w.mm - (uint8_t*)ws), stream);
+        if (e != hipSuccess) return e;
+    }
     if (block_m == 64)
         return launch_grouped_bm<64>(pa, gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
                                      pa.inter, out, stream);

@@ -169,7 +169,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // [block][K step][row].
 __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restrict__ sorted_pair,
                                                        const int32_t* __restrict__ block_slot,
-                                                       const uint8_t* __restrict__ fmt,
+                                                       const uint8_t* __restrict__ fmt, int n_slots, int fmt_ok,
                                                        const int32_t* __restrict__ n_padded, int NP, int k,
                                                        const float* __restrict__ topk_w,
                                                        const uint8_t* __restrict__ xs, int groups,
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
             int seg = carry;
             for (int w = 0; w < wv; ++w) seg = s_last[w] > seg ? s_last[w] : seg;
             if (smask & upto) seg = b0 + 64 * wv + 63 - __clzll(smask & upto);
-            const bool f = valid && slot >= 0 && fmt[slot] == 0;
+            const bool f = valid && usable_slot(slot, n_slots, fmt_ok, fmt) >= 0 && fmt[slot] == 0;
             const bool t = f && ((b - seg) & 1) == 0;
             const bool o = valid && !f;
             const int nblk = (t && b + 1 < nb && block_slot[b + 1] == slot) ? 2 : 1;
@@ -618,8 +618,8 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     if (nwg < 8) nwg = 8;
     if (phase == 0) {
         MOE_LAUNCH(K_MFMA_PREP, stream, mfma_prep_kernel, dim3(1 + (cap + 255) / 256), dim3(256), 0, stream,
-                   sorted_pair, block_slot, pa.fmt, n_padded, NP, k, topk_w, xs, H / 128, tiles, n_tiles, others,
-                   n_others, tokrow, wsort, scl);
+                   sorted_pair, block_slot, pa.fmt, pa.n_slots, pa.fmt_ok, n_padded, NP, k, topk_w, xs, H / 128, tiles,
+                   n_tiles, others, n_others, tokrow, wsort, scl);
         MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, scl};
         hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);

@@ -33,6 +33,8 @@ struct SlotView {
     size_t stride;         // bytes per slot
     const uint8_t* fmt;    // device u8[n_slots]
     size_t off[2][4];      // part offsets per format
+    int fmt_ok;            // bit f: format f fits the stride (usable_slot)
+    int spec_fmt;          // a format that fits: loads issued before a slot's tag is known
 };
 
 __device__ __forceinline__ void fp8x16_to_bf16(const i32x4& v, bf16x8& s0, bf16x8& s1) {
@@ -138,15 +140,16 @@ __global__ void __launch_bounds__(G_THREADS) gemm1_stream_kernel(
     const int groups = H / 128;
     // ---- round trip 1 (all inside the arrays: b < capacity / BM)
     const int npad = *n_padded;
-    const int slot = block_slot[b];
+    const int slot_in = block_slot[b];
     int pr[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pr[nt] = sorted_pair[b * BM + nt * 16 + m];
     for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
     __syncthreads();
+    const int slot = usable_slot(slot_in, n_slots, pool.fmt_ok, s_fmt);
     if (b >= npad / BM || slot < 0) return;           // uniform over the workgroup
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int fmt = (s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+    const int fmt = s_fmt[slot];
     const uint16_t* xr[NT];
     bool pv[NT];
 #pragma unroll
@@ -455,8 +458,8 @@ struct P1Range { int u_begin, u_end, b_first, nblk; };
 
 template <int RVPL, int RT>
 __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_t* __restrict__ fmt, int n_slots,
-                                                  int T, int k, int ntile, uint8_t* s_fmt, int* s_slot,
-                                                  int (*s_pr)[16]) {
+                                                  int fmt_ok, int spec_fmt, int T, int k, int ntile, uint8_t* s_fmt,
+                                                  int* s_slot, int (*s_pr)[16]) {
     __shared__ unsigned long long s_tok[MOE_MAX_E];  // bit t: token t chose the expert
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_off[MOE_MAX_E];
@@ -506,7 +509,6 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         if (e < E) {
             s_tok[e] = 0ull;
             s_cnt[e] = 0;
-            s_sl[e] = slot_e[i];
         }
     }
     if (tid < n_slots) s_fmt[tid] = (uint8_t)fv0;
@@ -538,6 +540,14 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         }
     }
     __syncthreads();
+    // the format tags are in LDS: a slot outside the pool or with a format
+    // that does not fit the stride counts as not resident
+#pragma unroll
+    for (int i = 0; i < LAYER_EPT; ++i) {
+        const int e = tid * LAYER_EPT + i;
+        slot_e[i] = usable_slot(slot_e[i], n_slots, fmt_ok, s_fmt);
+        if (e < E) s_sl[e] = slot_e[i];
+    }
     if constexpr (RVPL != 0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) pid[j] = tid + j * G_THREADS < NP ? s_ids[tid + j * G_THREADS] : -1;
@@ -638,8 +648,8 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
                     else hi = mid - 1;
                 }
                 slot = s_sl[lo];
-                f = slot >= 0 ? s_fmt[slot] : 0;
             }
+            f = slot >= 0 ? (int)s_fmt[slot] : spec_fmt;   // (slot -1: the down kernel loads slot 0 in this format)
             L.gdesc[g] = make_int4(ub, ue, slot, f);
         }
     }
@@ -677,7 +687,13 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     P1X X;
     int xblock = -1;
     int u_begin, u_end, b_first, nblk;
-    auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
+    // a block's slot if usable, else -1 (not resident, outside the pool, or a
+    // format that does not fit the stride)
+    auto ok = [&](int slot) { return usable_slot(slot, n_slots, pool.fmt_ok, s_fmt); };
+    // slot and format to load for a table entry: an unusable entry loads slot
+    // 0 in a format that fits the stride (its unit ignores the values)
+    auto pf_slot = [&](int slot) { return max(ok(slot), 0); };
+    auto pf_fmt = [&](int slot) { const int s = ok(slot); return s >= 0 ? (int)s_fmt[s] : pool.spec_fmt; };
     if constexpr (FUSE == 0) {
         const int n_units = (*n_padded / 16) * ntile;
         unit_range(n_units, gridDim.x, blockIdx.x, u_begin, u_end);
@@ -686,10 +702,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         if (nblk == 0) return;
         // ---- the descriptors of my blocks and the format tags, and the first
         // unit's weights, in one round trip. Loads complete in issue order, so
-        // the descriptor loads go first; the weights are loaded in the FP8
-        // layout before the slot's format is known (an int4 slot is at least
-        // as large, so the loads stay inside it) and loaded again if the slot
-        // is int4.
+        // the descriptor loads go first; the weights are loaded before the
+        // slot's format is known, from the table entry clamped into the pool
+        // and in a format whose layout fits the stride (so every load stays
+        // inside the pool), and loaded again if the slot's format differs.
         const int i0f = threadIdx.x;
         const int bb0 = i0f / 17, r0 = i0f % 17;
         uint8_t f0 = 0;
@@ -697,7 +713,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         if (i0f < n_slots) f0 = pool.fmt[i0f];
         if (i0f < nblk * 17) d0 = r0 == 16 ? block_slot[b_first + bb0] : sorted_pair[(b_first + bb0) * 16 + r0];
         __builtin_amdgcn_sched_barrier(0);          // keep the descriptor loads ahead of the weights
-        p1_issue_w(WA, pool, max(block_slot[b_first], 0), 0, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        p1_issue_w(WA, pool, min(max(block_slot[b_first], 0), n_slots - 1), pool.spec_fmt, (u_begin % ntile) * P1_ROWS,
+                   m, q, wv, H, I, groups);
         __builtin_amdgcn_sched_barrier(0);
         if (i0f < n_slots) s_fmt[i0f] = f0;
         if (i0f < nblk * 17) {
@@ -711,26 +728,28 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             else s_pr[bb][r] = sorted_pair[(b_first + bb) * 16 + r];
         }
         barrier_lds();                               // tables written; the weight loads stay in flight
-        if (fmt_of(s_slot[0]) == 1) {                // the first unit is int4: load it in its own layout
+        const int s0 = ok(s_slot[0]);
+        if (s0 >= 0 && s_fmt[s0] != pool.spec_fmt) {  // the first unit's format differs: load it in its own layout
             p1_landed(WA);
-            p1_issue_w(WA, pool, s_slot[0], 1, (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+            p1_issue_w(WA, pool, s0, s_fmt[s0], (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
     } else {
-        const P1Range R = layer_prologue<RVPL, RT>(L, pool.fmt, n_slots, T, k, ntile, s_fmt, s_slot, s_pr);
+        const P1Range R = layer_prologue<RVPL, RT>(L, pool.fmt, n_slots, pool.fmt_ok, pool.spec_fmt, T, k, ntile, s_fmt,
+                                                   s_slot, s_pr);
         u_begin = R.u_begin;
         u_end = R.u_end;
         b_first = R.b_first;
         nblk = R.nblk;
         if (nblk == 0) return;                       // uniform over the workgroup
         barrier_lds();
-        p1_issue_w(WA, pool, max(s_slot[0], 0), fmt_of(s_slot[0]), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I,
+        p1_issue_w(WA, pool, pf_slot(s_slot[0]), pf_fmt(s_slot[0]), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I,
                    groups);
     }
     auto step = [&](int u, P1W& Wc, P1W& Wn) {
         const int bb = u / ntile - b_first;
         const int i0 = (u % ntile) * P1_ROWS;
-        const int slot = s_slot[bb];
-        const int fmt = fmt_of(slot);
+        const int slot = ok(s_slot[bb]);
+        const int fmt = slot >= 0 ? (int)s_fmt[slot] : 0;
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != xblock) {              // new block: its token rows, before the prefetch
@@ -738,11 +757,11 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             xblock = bb;
         }
         {
-            // the next unit's weights (FP8 layout, also for an int4 or absent
-            // slot, whose unit ignores them; past the range: this unit again)
+            // the next unit's weights (slot 0 for an unusable slot, whose unit
+            // ignores them; past the range: this unit again)
             const int un = min(u + 1, u_end - 1);
-            const int sn = max(s_slot[un / ntile - b_first], 0);
-            p1_issue_w(Wn, pool, sn, fmt_of(sn), (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+            const int sn = s_slot[un / ntile - b_first];
+            p1_issue_w(Wn, pool, pf_slot(sn), pf_fmt(sn), (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
         // every path waits here for this unit's weight loads, so no load into
         // a register set is still pending when the set is refilled
@@ -806,13 +825,14 @@ __global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
     const int groups = I / MOE_INT4_G;
     // ---- round trip 1
     const int npad = *n_padded;
-    const int slot = block_slot[b];
+    const int slot_in = block_slot[b];
     int pr[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pr[nt] = sorted_pair[b * BM + nt * 16 + m];
     for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
     __syncthreads();
     if (b >= npad / BM) return;                       // uniform over the workgroup
+    const int slot = usable_slot(slot_in, n_slots, pool.fmt_ok, s_fmt);
     bool pv[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pv[nt] = pr[nt] < NP;
@@ -823,7 +843,7 @@ __global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
         return;
     }
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    const int fmt = (s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0;
+    const int fmt = s_fmt[slot];
     float wt[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) wt[nt] = pv[nt] ? topk_w[pr[nt]] : 0.f;
@@ -1018,7 +1038,11 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     }
     const int b_first = u_begin / ntile;
     const int nblk = u_begin < u_end ? (u_end - 1) / ntile - b_first + 1 : 0;
-    auto fmt_of = [&](int slot) { return (slot >= 0 && s_fmt[slot] == 1 && I % MOE_INT4_G == 0) ? 1 : 0; };
+    // usable slot or -1, and what to load for a table entry (an unusable one:
+    // slot 0 in a format that fits the stride; its unit ignores the values)
+    auto ok = [&](int slot) { return usable_slot(slot, n_slots, pool.fmt_ok, s_fmt); };
+    auto pf_slot = [&](int slot) { return max(ok(slot), 0); };
+    auto pf_fmt = [&](int slot) { const int s = ok(slot); return s >= 0 ? (int)s_fmt[s] : pool.spec_fmt; };
     P2W<P2_C> WA, WB;
     P2H<P2_C> Hh;
     int hblock = -1;
@@ -1028,15 +1052,14 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         // the tables, then the first unit's weights, in one round trip (loads
         // complete in issue order: the tables can be waited for while the
         // weights stay in flight; a non-resident first block reads slot 0's
-        // bytes and ignores them)
+        // bytes in a format that fits the stride and ignores them)
         const int i0 = threadIdx.x, i1 = threadIdx.x + G_THREADS;
         int f0 = 0, d0 = 0, d1 = 0;
         if (i0 < n_slots) f0 = pool.fmt[i0];
         if (i0 < nblk * 17) d0 = i0 % 17 == 16 ? block_slot[b_first + i0 / 17] : sorted_pair[(b_first + i0 / 17) * 16 + i0 % 17];
         if (i1 < nblk * 17) d1 = i1 % 17 == 16 ? block_slot[b_first + i1 / 17] : sorted_pair[(b_first + i1 / 17) * 16 + i1 % 17];
         __builtin_amdgcn_sched_barrier(0);
-        p2_issue_w(WA, pool, max(g_slot, 0), (g_fmt == 1 && I % MOE_INT4_G == 0) ? 1 : 0,
-                   (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        p2_issue_w(WA, pool, max(g_slot, 0), g_fmt, (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
         __builtin_amdgcn_sched_barrier(0);
         if (i0 < n_slots) s_fmt[i0] = (uint8_t)f0;
         if (i0 < nblk * 17) {
@@ -1059,27 +1082,28 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         __syncthreads();
         if (nblk == 0) return;
         const int s0 = s_slot[0];
-        p2_issue_w(WA, pool, max(s0, 0), fmt_of(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        p2_issue_w(WA, pool, pf_slot(s0), pf_fmt(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
     }
     auto step = [&](int u, P2W<P2_C>& Wc, P2W<P2_C>& Wn) {
         const int bb = u / ntile - b_first;
         const int n0 = (u % ntile) * G2_COLS + wv * 16;
-        const int slot = s_slot[bb];
+        const int slot = ok(s_slot[bb]);
+        const int fmt = slot >= 0 ? (int)s_fmt[slot] : 0;
         const int pr = s_pr[bb][m];
         const bool valid = pr < NP;
         if (slot >= 0 && bb != hblock) {              // new block: its h rows and route weights
-            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + (valid ? m : 0)) * I, fmt_of(slot), q, chunks);
+            p2_issue_h(Hh, hbuf + (size_t)((b_first + bb) * 16 + (valid ? m : 0)) * I, fmt, q, chunks);
             wt = topk_w[valid ? pr : 0];              // (used only where valid)
             hblock = bb;
         }
         {
             // the next unit's weights, with no branch around the loads (slot 0
-            // for a non-resident expert, whose unit ignores them; past the
-            // range: this unit again), so the compiler's count of loads in
-            // flight stays exact and the wait below leaves them in flight
+            // for an unusable slot, whose unit ignores them; past the range:
+            // this unit again), so the compiler's count of loads in flight
+            // stays exact and the wait below leaves them in flight
             const int un = min(u + 1, u_end - 1);
             const int sn = s_slot[un / ntile - b_first];
-            p2_issue_w(Wn, pool, max(sn, 0), fmt_of(sn), (un % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+            p2_issue_w(Wn, pool, pf_slot(sn), pf_fmt(sn), (un % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
         }
         // every path waits here for this unit's weight loads, so no load into
         // a register set is still pending when the set is refilled
@@ -1090,7 +1114,7 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
             return;
         }
         f32x4 acc = {0, 0, 0, 0};
-        if (fmt_of(slot) == 0) {
+        if (fmt == 0) {
 #pragma unroll
             for (int c = 0; c < P2_C; ++c) {
                 if (c >= chunks) break;                // uniform
@@ -1314,9 +1338,15 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
     sv.fmt = pa.fmt;
     for (int f = 0; f < 2; ++f)
         for (int p = 0; p < 4; ++p) sv.off[f][p] = pa.off[f][p];
+    sv.fmt_ok = pa.fmt_ok;
+    sv.spec_fmt = pa.spec_fmt;
     const int H = pa.hidden, I = pa.inter;
     uint16_t* hbuf = (uint16_t*)ws;
     float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
+    if (debug_poison_on()) {                          // h and y rows: NaN until written
+        hipError_t e = launch_poison(ws, stream_workspace_bytes(T, k, H, I, cap), stream);
+        if (e != hipSuccess) return e;
+    }
     switch (block_m) {
         case 16: launch_stream_bm<16>(sv, pa.n_slots, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf, stream); break;
         case 32: launch_stream_bm<32>(sv, pa.n_slots, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, H, I, hbuf, ybuf, stream); break;
@@ -1369,10 +1399,16 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
     sv.fmt = pa.fmt;
     for (int f = 0; f < 2; ++f)
         for (int p = 0; p < 4; ++p) sv.off[f][p] = pa.off[f][p];
+    sv.fmt_ok = pa.fmt_ok;
+    sv.spec_fmt = pa.spec_fmt;
     const int H = pa.hidden, I = pa.inter;
     uint16_t* hbuf = (uint16_t*)ws;
     float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
     int4* gdesc = (int4*)((uint8_t*)ws + stream_workspace_bytes(T, k, H, I, cap));
+    if (debug_poison_on()) {                          // h and y rows: NaN until written
+        hipError_t e = launch_poison(ws, stream_workspace_bytes(T, k, H, I, cap), stream);
+        if (e != hipSuccess) return e;
+    }
     LayerIO L{logits, mask,     slot_of_expert, E,          ids,         w,          sorted_pair,
               block_slot, counts, seg_offset, n_padded, err, gdesc, 2 * device_cus(), H};
     if (T <= LAYER_ROUTE_MAX_T && E <= 512) {

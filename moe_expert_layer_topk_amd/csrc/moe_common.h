@@ -18,6 +18,19 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 namespace moe {
 
+// Slot usability. fmt_ok has bit f set when format f's layout fits the pool
+// stride (and, for int4, when inter is a multiple of 128). A slot index is
+// usable when it lies inside the pool and its format tag is one of those;
+// anything else (a table entry past the pool, a tag other than FP8 or int4, a
+// format larger than the stride) is treated like a non-resident expert, so no
+// kernel reads outside the pool whatever the slot table or the tags hold.
+__device__ __forceinline__ bool fmt_usable(int tag, int fmt_ok) { return tag >= 0 && tag < 2 && ((fmt_ok >> tag) & 1); }
+template <typename TagPtr>
+__device__ __forceinline__ int usable_slot(int slot, int n_slots, int fmt_ok, TagPtr tags) {
+    if ((unsigned)slot >= (unsigned)n_slots) return -1;
+    return fmt_usable((int)tags[slot], fmt_ok) ? slot : -1;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // round-to-nearest-even fp32 -> bf16 (finite inputs)

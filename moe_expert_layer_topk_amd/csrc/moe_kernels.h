@@ -9,7 +9,7 @@ namespace moe {
 
 // kernel ids for launch tracing (names in profile.hip)
 enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
-                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_COUNT };
+                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_POOL_CHECK, K_POISON, K_COUNT };
 // events the next launch of kernel `kid` on `s` should stamp (false: not tracing)
 bool prof_events(int kid, hipStream_t s, hipEvent_t* start, hipEvent_t* stop);
 
@@ -30,6 +30,16 @@ struct PoolArgs {
     int n_slots;
     int hidden, inter;
     size_t off[2][4];   // byte offsets of the four arrays, per slot format
+    int fmt_ok;         // bit f: format f's layout fits the stride (int4 also needs inter % 128 == 0)
+    int spec_fmt;       // a format that fits: speculative loads before a slot's tag is known use it
+};
+
+// Optional check of slot-table entries against a pool (moe_layer passes one):
+// an entry outside the pool or whose format tag is unusable becomes -1.
+struct SlotCheck {
+    const uint8_t* fmt = nullptr;   // null: entries are copied as given
+    int n_slots = 0;
+    int fmt_ok = 0;
 };
 
 hipError_t launch_route(const float* logits, const uint8_t* mask, int T, int E, int k, int32_t* ids, float* w,
@@ -40,11 +50,11 @@ int route_align_fused_max_pairs();
 hipError_t launch_route_align(const float* logits, const uint8_t* mask, int T, int E, int k, int block_m,
                               const int32_t* slot_of_expert, int32_t* ids, float* w, int32_t* sorted_pair,
                               int32_t* block_slot, int32_t* counts, int32_t* seg_offset, int32_t* n_padded,
-                              int32_t* err, void* ws, hipStream_t stream);
+                              int32_t* err, void* ws, hipStream_t stream, SlotCheck chk = SlotCheck());
 size_t align_workspace_bytes(int NP, int E);
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, const int32_t* slot_of_expert,
                         int32_t* sorted_pair, int32_t* block_slot, int32_t* counts, int32_t* seg_offset,
-                        int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream);
+                        int32_t* n_padded, int32_t* err, void* ws, hipStream_t stream, SlotCheck chk = SlotCheck());
 
 int stream_max_tokens();
 int device_cus();
@@ -81,5 +91,17 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
                            int phase, hipStream_t stream);
 
 hipError_t launch_dequant(const PoolArgs& pa, int slot, float* w13, float* w2, hipStream_t stream);
+
+// activation quantization alone: e4m3 codes [rows][cols], E8M0 bytes [rows][cols / 128]
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* exps, hipStream_t stream);
+
+// pool validation (pool_check.hip): d_err += unusable slots; status[slot] optional
+hipError_t launch_pool_check(const PoolArgs& pa, int32_t* err, uint8_t* status, hipStream_t stream);
+
+// debug mode: fill workspace data regions with all-ones bytes (NaN in every
+// float format used) before the FFN kernels run
+void set_debug_poison(int on);
+bool debug_poison_on();
+hipError_t launch_poison(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace moe

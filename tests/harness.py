@@ -31,6 +31,14 @@ def device_pool(li, bank, dev, bank_dev=None):
     return SlotPool(data, fmt, c.H, c.I)
 
 
+def SlotPool_from_host(host, slot_fmt, hidden, inter, dev):
+    """A pool from host bytes uint8 [n_slots, stride] and per-slot tags."""
+    import torch
+    from moe_expert_layer_topk_amd import SlotPool
+    return SlotPool(torch.from_numpy(np.ascontiguousarray(host)).to(dev), torch.from_numpy(slot_fmt.copy()).to(dev),
+                    hidden, inter)
+
+
 def bank_on_device(bank, dev):
     import torch
     return {f: torch.from_numpy(bank.materialize(f)).to(dev) for f in bank.fmts}
@@ -43,6 +51,21 @@ def device_inputs(li, dev):
     soe = torch.from_numpy(li.slot_of_expert.copy()).to(dev)
     mask = None if li.mask is None else torch.from_numpy(li.mask.copy()).to(dev)
     return x, logits, soe, mask
+
+
+class BoundedCache(dict):
+    """A dict that keeps only its `size` most recent entries (the oracle walks
+    blocks in ascending expert order, so one decoded expert at a time is
+    enough and keeps host memory bounded at full-size layers)."""
+
+    def __init__(self, size=2):
+        super().__init__()
+        self.size = size
+
+    def __setitem__(self, key, value):
+        while len(self) >= self.size:
+            del self[next(iter(self))]
+        super().__setitem__(key, value)
 
 
 class OracleSlots:

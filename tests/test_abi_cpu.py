@@ -44,6 +44,17 @@ def test_slot_layout_matches_generator(L, name):
             assert moe.slot_part_offset(c.H, c.I, fmt, i) == lay[p][0]
 
 
+def test_slot_bytes_hand_values(L):
+    """Slot sizes at hidden 2048, inter 512, worked by hand from the layout:
+    FP8 = 2I*H codes + 2I*4 scale + H*I codes + H*4 scale = 2097152 + 4096 +
+    1048576 + 8192 = 3158016 (each array already a multiple of 256); int4 =
+    I*H + 2I*(H/128)*4 + H*I/2 + H*(I/128)*4 = 1048576 + 65536 + 524288 +
+    32768 = 1671168, plus the 16 spare tail bytes rounded up to 256."""
+    assert moe.slot_bytes(2048, 512, 0) == 3158016
+    assert moe.slot_bytes(2048, 512, 1) == 1671168 + 256
+    assert moe.slot_bytes(2048, 768, 0) == 2 * 768 * 2048 + 2 * 768 * 4 + 2048 * 768 + 2048 * 4   # 4732928
+
+
 def test_align_capacity_formula(L):
     import oracle
     for T, k, E, bm in [(1, 8, 256, 16), (32, 8, 256, 16), (16384, 8, 256, 128), (7, 3, 5, 64), (16, 2, 8, 256)]:
@@ -74,6 +85,14 @@ def test_host_checks_reject_bad_arguments(L):
     assert L.moe_expert_ffn(ctypes.byref(pool), *big_t, 16, 0, fake, fake, 1 << 40, null) == -1   # bf16 T > 64
     assert L.moe_dequant_slot(ctypes.byref(pool), 4, fake, fake, null) == -1                     # slot range
     assert L.moe_dequant_slot(ctypes.byref(pool), 0, null, null, null) == -1
+    assert L.moe_quant_act(fake, 4, 100, fake, fake, null) == -1                                  # cols % 128
+    assert L.moe_quant_act(fake, 0, 256, fake, fake, null) == -1
+    assert L.moe_pool_check(ctypes.byref(small), fake, null, null) == -1                          # stride
+    assert L.moe_pool_check(ctypes.byref(pool), null, null, null) == -1                           # no err word
+    int4_only = moe.binding.moe_slot_pool(fake, moe.slot_bytes(2048, 512, 1), 4, fake, 2048, 512)
+    one_short = moe.binding.moe_slot_pool(fake, moe.slot_bytes(2048, 512, 1) - 256, 4, fake, 2048, 512)
+    assert L.moe_dequant_slot(ctypes.byref(one_short), 0, fake, fake, null) == -1                 # fits no format
+    assert L.moe_dequant_slot(ctypes.byref(int4_only), 4, fake, fake, null) == -1                 # (slot range)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

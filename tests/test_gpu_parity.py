@@ -349,15 +349,38 @@ def test_layer_call_batched_falls_back(gpu):
     run_layer_call(make_layer(MID, 300, 0), make_bank(MID), gpu, 64, 1)
 
 
+def block_complete_tokens(li, block_m):
+    """Tokens whose rows cover every align block of the layer: for each block,
+    the tokens of its first and its last real row (a segment's last, partial
+    block included), taken from the oracle's own route and align."""
+    c = li.cfg
+    ids, _, _ = oracle.route(li.logits, li.mask, c.k)
+    al = oracle.align(ids, c.E, block_m, li.slot_of_expert)
+    NP, sp = li.T * c.k, al["sorted_pair"]
+    toks = set()
+    for b in range(al["n_padded"] // block_m):
+        rows = sp[b * block_m:(b + 1) * block_m]
+        real = rows[rows < NP]
+        if real.size:
+            toks.update((int(real[0]) // c.k, int(real[-1]) // c.k))
+    return np.array(sorted(toks)), al["n_padded"] // block_m
+
+
 @pytest.mark.parametrize("name,T,block_m", [("C2", 16384, 128), ("C4", 8192, 128), ("C3", 4096, 128)])
-def test_layer_batched_full_size_sampled(gpu, name, T, block_m):
+def test_layer_batched_full_size_every_block(gpu, name, T, block_m):
+    """Full-size batched layers in the launch configuration the benchmark
+    times, compared on every element of a token set that reaches every
+    128-row block (first and last real row of each), so every tile, every
+    segment's partial last block and every int4 block is checked."""
+    from harness import BoundedCache
     c = CONFIGS[name]
     bank = make_bank(c)
     _say(f"[bank] {name}: generating {bank.n} experts")
     bdev = bank_on_device(bank, gpu)
     li = make_layer(c, T, 0)
-    sample = np.random.default_rng(T).choice(T, 48, replace=False)
-    run_layer(li, bank, gpu, block_m, 1, sample=sample, bank_dev=bdev)
+    sample, n_blocks = block_complete_tokens(li, block_m)
+    _say(f"    {sample.size} of {T} tokens cover all {n_blocks} blocks")
+    run_layer(li, bank, gpu, block_m, 1, sample=sample, bank_dev=bdev, cache=BoundedCache())
 
 
 # ---------------------------------------------------------------- dequant
