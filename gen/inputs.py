@@ -218,6 +218,16 @@ def zipf_prior(cfg: Config, T: int, layer: int) -> np.ndarray:
     return p / p.sum()
 
 
+def router_inputs(cfg: Config, T: int, layer: int):
+    """The router gate of one layer as fp32 arrays: W_g [E, H] (the layer's
+    N(0, wg_std) draw rounded to fp32) and bias [E] (the log-Zipf prior, or
+    zeros), for the token rows of make_layer(cfg, T, layer)."""
+    c = cfg
+    Wg = _rng(c.cfg_id, T, layer, "Wg").standard_normal((c.E, c.H)) * c.wg_std
+    bias = np.log(zipf_prior(c, T, layer)) if c.zipf else np.zeros(c.E)
+    return Wg.astype(np.float32), bias.astype(np.float32)
+
+
 def make_layer(cfg: Config, T: int, layer: int) -> LayerInputs:
     c = cfg
     E, H, k = c.E, c.H, c.k

@@ -73,6 +73,22 @@ int         moe_last_hip_error(void);
 int moe_route(const float* d_logits, const uint8_t* d_mask, int T, int E, int k,
               int32_t* d_topk_ids, float* d_topk_w, int32_t* d_err, void* stream);
 
+/* Route from the token rows: the router gate first, then moe_route.
+ * [PW] "technically interesting points": the router picks each token's
+ * experts. d_logits[t][e] = sum_h x[t][h] * W_g[e][h] + bias[e] in fp32:
+ * W_g is split exactly into three bf16 parts, so every product is exact and
+ * the result differs from the exact logit only by the rounding of the fp32
+ * sum (at most gamma_{3H} sum_h |x W| + one rounding of the bias add); the
+ * order of that sum is fixed, so results repeat from run to run. The logits
+ * are written (the caller keeps them) and then routed exactly as moe_route
+ * routes them.
+ *  d_x bf16 [T, H]; d_wg f32 [E, H]; d_bias f32 [E] or NULL; d_mask as in
+ *  moe_route; d_logits f32 [T, E] (output); the rest as in moe_route.
+ * Limits: H a multiple of 128; the rest as in moe_route. */
+int moe_route_gemm(const uint16_t* d_x, const float* d_wg, const float* d_bias, const uint8_t* d_mask, int T, int H,
+                   int E, int k, float* d_logits, int32_t* d_topk_ids, float* d_topk_w, int32_t* d_err,
+                   void* stream);
+
 /* ---------------------------------------------------------------- align
  * [MG] sections 1 and 3: tokens are grouped per expert module so each expert
  * runs one large batch. [VEP] "hierarchical paging of expert weights": each
@@ -214,6 +230,25 @@ int moe_quant_act(const uint16_t* d_x, int rows, int cols, uint8_t* d_codes, uin
  * q - zero exactly only for such zero points), 4 an FP8 row scale that is
  * not finite. d_err i32 [1] gets +1 per slot with a nonzero status. */
 int moe_pool_check(const moe_slot_pool* pool, int32_t* d_err, uint8_t* d_status, void* stream);
+
+/* ---------------------------------------------------------------- bit width
+ * [PW] "technically interesting points": each expert is held at a bit width
+ * chosen by how much it matters, switched while the model serves.
+ * moe_bitwidth_plan (host arrays, no GPU): fmt_out[e] = MOE_FMT_INT4_G128 for
+ * the n_int4 experts with the fewest routed pairs (counts as moe_align
+ * writes them; ties to the lower expert id), MOE_FMT_FP8_E4M3_ROW otherwise.
+ * moe_requant_slot: the expert in FP8 slot src_slot is requantized into slot
+ * dst_slot of the same pool in int4-g128, and d_slot_fmt[dst_slot] is set to
+ * MOE_FMT_INT4_G128 (the source slot is left as it is). Per row and group of
+ * 128 K values w = e4m3(code) * row_scale (fp32): s = fp16((max - min) / 15)
+ * (1 when 0), zero = clip(rint(-min / s), 0, 15), q = clip(rint(w / s) +
+ * zero, 0, 15), every step in fp32 with IEEE rounding (ties to even), so the
+ * bytes written are fully determined. If src_slot is not a usable FP8 slot
+ * nothing is written and d_err (i32 [1], may be NULL) gets +1. Both formats
+ * must fit slot_bytes; src_slot != dst_slot. The caller points the expert's
+ * slot-table entry at dst_slot when it wants the int4 copy used. */
+int moe_bitwidth_plan(const int32_t* counts, int E, int n_int4, uint8_t* fmt_out);
+int moe_requant_slot(const moe_slot_pool* pool, int src_slot, int dst_slot, int32_t* d_err, void* stream);
 
 /* ---------------------------------------------------------------- debug
  * moe_debug_poison(1): every later FFN call (moe_expert_ffn, moe_layer)

@@ -39,6 +39,7 @@ def _declare(lib):
         "moe_last_hip_error": (c_int, []),
         "moe_route": (c_int, [P, P, c_int, c_int, c_int, P, P, P, P]),
         "moe_align_capacity": (c_int, [c_int, c_int, c_int, c_int]),
+        "moe_route_gemm": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, P, P, P, P, P]),
         "moe_align_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "moe_align": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P, P, c_size_t, P]),
         "moe_route_align_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -55,6 +56,8 @@ def _declare(lib):
         "moe_quant_act": (c_int, [P, c_int, c_int, P, P, P]),
         "moe_pool_check": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P]),
         "moe_debug_poison": (c_int, [c_int]),
+        "moe_bitwidth_plan": (c_int, [P, c_int, c_int, P]),
+        "moe_requant_slot": (c_int, [ctypes.POINTER(moe_slot_pool), c_int, c_int, P, P]),
         "moe_profile_enable": (c_int, [c_int]),
         "moe_profile_kernels": (c_int, []),
         "moe_profile_kernel_name": (ctypes.c_char_p, [c_int]),
@@ -130,6 +133,23 @@ def route(logits, k, mask=None, ids=None, w=None, err=None, stream=None):
                            _ptr(ids, torch.int32, T * k, "ids"), _ptr(w, torch.float32, T * k, "w"),
                            _ptr(err, torch.int32, 1, "err"), _stream(stream)))
     return ids, w, err
+
+
+def route_gemm(x, W_g, k, bias=None, mask=None, logits=None, ids=None, w=None, err=None, stream=None):
+    """moe_route_gemm: router gate GEMM then top-k. Returns (logits, ids, w, err)."""
+    import torch
+    T, H = x.shape
+    E = W_g.shape[0]
+    dev = x.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if logits is None else logits
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    err = torch.zeros(1, dtype=torch.int32, device=dev) if err is None else err
+    _check(lib().moe_route_gemm(_ptr(x, torch.bfloat16, T * H, "x"), _ptr(W_g, torch.float32, E * H, "W_g"),
+                                _ptr(bias, torch.float32, E, "bias"), _ptr(mask, torch.uint8, E, "mask"), T, H, E, k,
+                                _ptr(logits, torch.float32, T * E, "logits"), _ptr(ids, torch.int32, T * k, "ids"),
+                                _ptr(w, torch.float32, T * k, "w"), _ptr(err, torch.int32, 1, "err"), _stream(stream)))
+    return logits, ids, w, err
 
 
 # ---------------------------------------------------------------- align
@@ -297,6 +317,21 @@ def pool_check(pool, err=None, status=None, stream=None):
     _check(lib().moe_pool_check(pool.c_ref(), _ptr(err, torch.int32, 1, "err"),
                                 _ptr(status, torch.uint8, pool.n_slots, "status"), _stream(stream)))
     return err, status
+
+
+def bitwidth_plan(counts, n_int4):
+    """moe_bitwidth_plan on host arrays: counts int32 [E] -> uint8 [E] of formats."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    out = np.empty(c.size, dtype=np.uint8)
+    _check(lib().moe_bitwidth_plan(c.ctypes.data_as(c_void_p), c.size, int(n_int4), out.ctypes.data_as(c_void_p)))
+    return out
+
+
+def requant_slot(pool, src_slot, dst_slot, err=None, stream=None):
+    import torch
+    _check(lib().moe_requant_slot(pool.c_ref(), int(src_slot), int(dst_slot),
+                                  _ptr(err, torch.int32, 1, "err") if err is not None else None, _stream(stream)))
 
 
 def debug_poison(on=True):

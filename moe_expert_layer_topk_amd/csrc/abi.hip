@@ -109,6 +109,16 @@ int moe_route(const float* d_logits, const uint8_t* d_mask, int T, int E, int k,
     return hip_status(moe::launch_route(d_logits, d_mask, T, E, k, d_topk_ids, d_topk_w, d_err, (hipStream_t)stream));
 }
 
+int moe_route_gemm(const uint16_t* d_x, const float* d_wg, const float* d_bias, const uint8_t* d_mask, int T, int H,
+                   int E, int k, float* d_logits, int32_t* d_topk_ids, float* d_topk_w, int32_t* d_err, void* stream) {
+    if (!d_x || !d_wg || !d_logits || !d_topk_ids || !d_topk_w || !d_err) return MOE_EINVAL;
+    if (T < 1 || H < 128 || H % 128 || E < 1 || E > MOE_MAX_E || k < 1 || k > E || k > MOE_MAX_K) return MOE_EINVAL;
+    clear_stale_error();
+    hipError_t e = moe::launch_router_gemm(d_x, d_wg, d_bias, T, H, E, d_logits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(moe::launch_route(d_logits, d_mask, T, E, k, d_topk_ids, d_topk_w, d_err, (hipStream_t)stream));
+}
+
 int moe_align_capacity(int T, int k, int E, int block_m) {
     if (T < 1 || k < 1 || E < 1 || !valid_block_m(block_m)) return MOE_EINVAL;
     if ((long long)T * k >= (1LL << 30)) return MOE_EINVAL;
@@ -273,6 +283,17 @@ int moe_pool_check(const moe_slot_pool* pool, int32_t* d_err, uint8_t* d_status,
     if (!pool_args(pool, &pa) || !d_err) return MOE_EINVAL;
     clear_stale_error();
     return hip_status(moe::launch_pool_check(pa, d_err, d_status, (hipStream_t)stream));
+}
+
+int moe_requant_slot(const moe_slot_pool* pool, int src_slot, int dst_slot, int32_t* d_err, void* stream) {
+    moe::PoolArgs pa;
+    if (!pool_args(pool, &pa)) return MOE_EINVAL;
+    if ((pa.fmt_ok & 3) != 3) return MOE_EINVAL;                 // both formats must fit the stride
+    if (src_slot < 0 || src_slot >= pa.n_slots || dst_slot < 0 || dst_slot >= pa.n_slots || src_slot == dst_slot)
+        return MOE_EINVAL;
+    clear_stale_error();
+    return hip_status(moe::launch_requant(pa, src_slot, dst_slot, (uint8_t*)pool->d_slot_fmt, d_err,
+                                          (hipStream_t)stream));
 }
 
 int moe_debug_poison(int on) {

@@ -9,7 +9,7 @@ namespace moe {
 
 // kernel ids for launch tracing (names in profile.hip)
 enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
-                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_POOL_CHECK, K_POISON, K_COUNT };
+                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_POOL_CHECK, K_POISON, K_ROUTER_GEMM, K_REQUANT, K_COUNT };
 // events the next launch of kernel `kid` on `s` should stamp (false: not tracing)
 bool prof_events(int kid, hipStream_t s, hipEvent_t* start, hipEvent_t* stop);
 
@@ -41,6 +41,10 @@ struct SlotCheck {
     int n_slots = 0;
     int fmt_ok = 0;
 };
+
+// router gate GEMM (router.hip): logits = x W_g^T + bias in fp32
+hipError_t launch_router_gemm(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E,
+                              float* logits, hipStream_t stream);
 
 hipError_t launch_route(const float* logits, const uint8_t* mask, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* err, hipStream_t stream);
@@ -97,6 +101,9 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* code
 
 // pool validation (pool_check.hip): d_err += unusable slots; status[slot] optional
 hipError_t launch_pool_check(const PoolArgs& pa, int32_t* err, uint8_t* status, hipStream_t stream);
+
+// FP8 slot src -> int4-g128 slot dst of the same pool (requant.hip); tags[dst] set to int4
+hipError_t launch_requant(const PoolArgs& pa, int src, int dst, uint8_t* tags, int32_t* err, hipStream_t stream);
 
 // debug mode: fill workspace data regions with all-ones bytes (NaN in every
 // float format used) before the FFN kernels run

@@ -38,6 +38,13 @@ MUTANTS = {
     "pow2_scale_too_large": ("numerics.py", "s[nz] = np.ceil(np.log2(amax[nz] / 448.0)).astype(np.int64)",
                              "s[nz] = np.ceil(np.log2(amax[nz] / 448.0)).astype(np.int64) + 3"),
     "act_group_wrong": ("numerics.py", "ACT_GROUP = 128", "ACT_GROUP = 64"),
+    "router_bias_dropped": ("router.py", "out = out + np.asarray(bias", "out = out + 0 * np.asarray(bias"),
+    "router_bias_sign": ("router.py", "out = out + np.asarray(bias", "out = out - np.asarray(bias"),
+    "router_x_not_decoded": ("router.py", "x = bf16_decode(x_bits)", "x = np.asarray(x_bits, dtype=np.float64)"),
+    "requant_divisor_16": ("requant.py", "(mx - mn) / np.float32(15.0)", "(mx - mn) / np.float32(16.0)"),
+    "requant_zero_sign": ("requant.py", "np.rint((-mn) / s32)", "np.rint(mn / s32)"),
+    "requant_nibble_order": ("requant.py", "(q[:, 0::2] | (q[:, 1::2] << 4))", "(q[:, 1::2] | (q[:, 0::2] << 4))"),
+    "plan_ties_to_higher_id": ("requant.py", "key=lambda e: (int(counts[e]), e)", "key=lambda e: (int(counts[e]), -e)"),
 }
 
 
@@ -149,7 +156,48 @@ def pin_dense_C0(m):
     return True
 
 
-PINS = [pin_e4m3, pin_route, pin_align, pin_ffn, pin_slots, pin_act_quant, pin_dense_C0]
+def pin_router(m):
+    g = kv("router_tiny.txt")
+    f = lambda key: [float(v) for v in g[key]]
+    from gen import bf16_round
+    x = np.array([f("x0"), f("x1")], dtype=np.float32)
+    W = np.array([f("w0"), f("w1"), f("w2")], dtype=np.float32)
+    out = m.router_logits(bf16_round(x), W, np.array(f("bias"), dtype=np.float32))
+    return out.tolist() == [f("out0"), f("out1")]
+
+
+def pin_integer_layer(m):
+    """The integer-valued layer against int64 arithmetic (test_oracle_exact)."""
+    from gen import make_integer_layer
+    from test_oracle_exact import integer_reference
+    li, bank, x_int = make_integer_layer(256, 128, 8, 4, 24)
+    pool = np.zeros((li.n_slots, bank.stride), dtype=np.uint8)
+    for s in range(li.n_slots):
+        b = bank.slot(li.slot_src[s], li.slot_fmt[s])
+        pool[s, :b.size] = b
+    want = integer_reference(li, bank, x_int)
+    for act in (0, 1):
+        r = m.layer_forward(li.logits, None, 4, li.slot_of_expert, pool, li.slot_fmt, 256, 128, li.x_bits, 16, act)
+        if not np.array_equal(r["out"], want):
+            return False
+    return True
+
+
+def pin_requant(m):
+    from test_oracle_requant import test_requant_reproduces_a_grid_exact_slot, test_plan_least_routed_ties_to_lower_id
+    import test_oracle_requant as tr
+    saved = tr.oracle
+    tr.oracle = m
+    try:
+        test_requant_reproduces_a_grid_exact_slot()
+        test_plan_least_routed_ties_to_lower_id()
+    finally:
+        tr.oracle = saved
+    return True
+
+
+PINS = [pin_e4m3, pin_route, pin_align, pin_ffn, pin_slots, pin_act_quant, pin_dense_C0, pin_router,
+        pin_integer_layer, pin_requant]
 
 
 def all_pins_pass(m):
