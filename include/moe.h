@@ -39,7 +39,7 @@ extern "C" {
 
 #define MOE_ABI_VERSION 1
 
-enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EHIP = -2 };
+enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EHIP = -2, MOE_ESCRATCH = -3 };
 
 /* Slot storage formats ([PW] "technically interesting points": each expert is
  * held at its own bit width; [VEP] introduction: official FP8 weights). */
@@ -259,6 +259,26 @@ int moe_requant_slot(const moe_slot_pool* pool, int src_slot, int dst_slot, int3
  * debugging aid (one extra fill per call); moe_debug_poison(0) turns it off.
  * Process-wide. */
 int moe_debug_poison(int on);
+
+/* ---------------------------------------------------------------- whole layer, no allocation
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, hosts that forbid
+ * allocation): moe_layer with the same arguments and results, minus d_ws and
+ * ws_bytes. Its workspace is a fixed array inside the library, one per GPU,
+ * of MOE_NOALLOC_SCRATCH_BYTES bytes, held until the process ends; the call
+ * allocates nothing. Layers whose moe_layer_workspace_bytes exceeds that
+ * size are refused with MOE_ESCRATCH (every decode-sized layer fits: T <= 64
+ * tokens with 16-pair blocks and bf16 activations need at most 16 MiB at
+ * hidden 2048, inter 768, 1024 experts). All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_noalloc(const moe_slot_pool* pool, const float* d_logits, const uint8_t* d_mask,
+                      const uint16_t* d_x, int T, int E, int k, int block_m, int act_mode,
+                      const int32_t* d_slot_of_expert, int32_t* d_topk_ids, float* d_topk_w,
+                      int32_t* d_sorted_pair, int32_t* d_block_slot, int32_t* d_counts,
+                      int32_t* d_seg_offset, int32_t* d_n_padded, int32_t* d_err, uint16_t* d_out,
+                      void* stream);
 
 /* ---------------------------------------------------------------- dequant
  * [PW] "technically interesting points": per-expert bit width. Writes the

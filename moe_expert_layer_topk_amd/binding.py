@@ -50,6 +50,8 @@ def _declare(lib):
         "moe_expert_ffn": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
                                    c_int, c_int, P, P, c_size_t, P]),
         "moe_layer_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+        "moe_layer_noalloc": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, c_int, c_int, c_int, c_int, c_int,
+                                      P, P, P, P, P, P, P, P, P, P, P]),
         "moe_layer": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, c_int, c_int, c_int, c_int, c_int, P,
                               P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "moe_dequant_slot": (c_int, [ctypes.POINTER(moe_slot_pool), c_int, P, P, P]),
@@ -389,6 +391,36 @@ def layer_call(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None,
                            _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
                            _ptr(err, torch.int32, 2, "err"), _ptr(out, torch.bfloat16, T * H, "out"),
                            _ptr(ws, torch.uint8, need, "ws"), c_size_t(ws.numel()), _stream(stream)))
+    aligned = dict(aligned)
+    aligned["err"] = err
+    return out, ids, w, aligned
+
+
+def layer_call_noalloc(pool, x, logits, k, slot_of_expert, block_m, act_mode, mask=None, ids=None, w=None,
+                       aligned=None, err=None, out=None, stream=None):
+    """moe_layer_noalloc: moe_layer with the library's built-in scratch as its
+    workspace. Returns (out, ids, w, aligned dict) like layer_call."""
+    import torch
+    T, H = x.shape
+    E = logits.shape[1]
+    dev = x.device
+    cap = align_capacity(T, k, E, block_m)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    aligned = _align_out(T, k, E, block_m, dev) if aligned is None else aligned
+    err = torch.zeros(2, dtype=torch.int32, device=dev) if err is None else err
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check(lib().moe_layer_noalloc(pool.c_ref(), _ptr(logits, torch.float32, T * E, "logits"),
+                                   _ptr(mask, torch.uint8, E, "mask"), _ptr(x, torch.bfloat16, T * H, "x"), T, E, k,
+                                   block_m, act_mode, _ptr(slot_of_expert, torch.int32, E, "slot_of_expert"),
+                                   _ptr(ids, torch.int32, T * k, "ids"), _ptr(w, torch.float32, T * k, "w"),
+                                   _ptr(aligned["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                                   _ptr(aligned["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                                   _ptr(aligned["counts"], torch.int32, E, "counts"),
+                                   _ptr(aligned["seg_offset"], torch.int32, E + 1, "seg_offset"),
+                                   _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
+                                   _ptr(err, torch.int32, 2, "err"), _ptr(out, torch.bfloat16, T * H, "out"),
+                                   _stream(stream)))
     aligned = dict(aligned)
     aligned["err"] = err
     return out, ids, w, aligned

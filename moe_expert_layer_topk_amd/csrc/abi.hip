@@ -23,6 +23,15 @@ int hip_status(hipError_t e) {
 
 size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 
+}  // namespace
+
+int moe::record_hip_error(int hip_error) {
+    g_last_hip = hip_error;
+    return MOE_EHIP;
+}
+
+namespace {
+
 bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 // Byte offsets of the four arrays of a slot (each 256-byte aligned).
@@ -95,6 +104,7 @@ const char* moe_strerror(int status) {
         case MOE_OK: return "ok";
         case MOE_EINVAL: return "invalid argument";
         case MOE_EHIP: return "HIP launch error";
+        case MOE_ESCRATCH: return "workspace needed exceeds moe_layer_noalloc's built-in scratch";
         default: return "unknown status";
     }
 }
