@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--calls", choices=("layer", "split"), default="layer",
                     help="layer: one moe_layer call per layer; split: moe_route_align then moe_expert_ffn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pager", action="store_true", help="leave out the slot-miss path record")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget of the headline workload")
     ap.add_argument("--cpu-seconds-records", type=float, default=5.0, help="... of each other record")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -316,6 +317,106 @@ def measure(args, name, T, L, cpu_seconds, mfma_bound):
     return rec
 
 
+def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
+    """The slot-miss path over a decode loop: each layer's VRAM pool holds
+    n_slots experts, every expert sits in page-locked host RAM, each step
+    brings new tokens (the layer's gate and reuse prior fixed). Per layer and
+    step: route, read the ids back, plan with the pager, fill the misses on a
+    copy stream while the resident experts' pass runs, then the filled
+    experts' pass. Step 0 starts from empty pools; the timed steps are 1..."""
+    import torch
+    import moe_expert_layer_topk_amd as moe
+    from gen import CONFIGS, make_bank, step_tokens
+
+    cfg = CONFIGS[name]
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    bank = make_bank(cfg)
+    host = torch.from_numpy(bank.materialize(0)).pin_memory()
+    host_fmt = torch.zeros(E, dtype=torch.uint8).pin_memory()
+    pools = [moe.SlotPool(torch.zeros((n_slots, bank.stride), dtype=torch.uint8, device=dev),
+                          torch.zeros(n_slots, dtype=torch.uint8, device=dev), H, I) for _ in range(L)]
+    inputs = []
+    for st in range(steps):
+        row = []
+        for l in range(L):
+            xb, lg = step_tokens(cfg, T, l, st)
+            row.append((torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16),
+                        torch.from_numpy(lg).to(dev)))
+        inputs.append(row)
+    pager = moe.Pager(L, E, n_slots)
+    ws = torch.empty(moe.ffn_workspace_bytes(T, k, E, H, I, 16, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids_h = torch.empty((T, k), dtype=torch.int32).pin_memory()
+    t1h = torch.empty(E, dtype=torch.int32).pin_memory()
+    t2h = torch.empty(E, dtype=torch.int32).pin_memory()
+    t1d = torch.empty(E, dtype=torch.int32, device=dev)
+    t2d = torch.empty(E, dtype=torch.int32, device=dev)
+    comp = torch.cuda.Stream()
+    copy = torch.cuda.Stream()
+    torch.cuda.set_stream(comp)
+    torch.cuda.synchronize()
+    log(f"[bench] pager {name} T={T} layers={L} slots={n_slots}: inputs ready in {time.time() - t0:.1f}s")
+    stats = dict(bytes=0, fill_ms=0.0, misses=0, hits=0)
+
+    def run_step(st, timed):
+        for l in range(L):
+            x, logits = inputs[st][l]
+            ids, w, _ = moe.route(logits, k, stream=comp)
+            ids_h.copy_(ids, non_blocking=True)
+            comp.synchronize()
+            table, fe, fs = pager.plan(l, ids_h.numpy())
+            miss = np.zeros(E, bool)
+            miss[fe] = True
+            t1h.numpy()[:] = np.where(miss, moe.SLOT_DEFERRED, table)
+            t2h.numpy()[:] = np.where(miss, table, moe.SLOT_DEFERRED)
+            copy.wait_stream(comp)                       # earlier kernels may still read the victim slots
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(copy)
+            moe.pager_fill(pools[l], host, host_fmt, fe, fs, copy)
+            c1.record(copy)
+            t1d.copy_(t1h, non_blocking=True)
+            t2d.copy_(t2h, non_blocking=True)
+            a1 = moe.align(ids, E, 16, t1d, stream=comp)
+            moe.expert_ffn_pass(pools[l], x, k, E, w, a1, 16, 0, False, out, ws, stream=comp)
+            comp.wait_event(c1)
+            a2 = moe.align(ids, E, 16, t2d, stream=comp)
+            moe.expert_ffn_pass(pools[l], x, k, E, w, a2, 16, 0, True, out, ws, stream=comp)
+            if timed:
+                c1.synchronize()
+                stats["fill_ms"] += c0.elapsed_time(c1)
+                stats["bytes"] += int(fe.size) * bank.stride
+                stats["misses"] += int(fe.size)
+                stats["hits"] += int(len(set(ids_h.numpy().reshape(-1).tolist())) - fe.size)
+
+    run_step(0, False)                                   # cold pools
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for st in range(1, steps):
+        run_step(st, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    n = (steps - 1) * L
+    layer_us = wall / n * 1e6
+    rec = dict(
+        workload=f"{name} slot-miss path: T={T} tokens x {L} layers, {n_slots} VRAM slots per layer, all {E} experts "
+                 f"in page-locked host RAM, new tokens every step",
+        value=round(T * n / wall, 1), tokens_per_layer=T, layers=L, steps_timed=steps - 1, vram_slots=n_slots,
+        layer_us=round(layer_us, 2), hit_rate=round(stats["hits"] / max(1, stats["hits"] + stats["misses"]), 4),
+        misses_per_layer_step=round(stats["misses"] / n, 2),
+        h2d_GBps=round(stats["bytes"] / max(1e-9, stats["fill_ms"] / 1e3) / 1e9, 2),
+        h2d_bytes_per_layer_step=int(stats["bytes"] / n),
+        fill_us_per_layer_step=round(stats["fill_ms"] / n * 1e3, 2),
+        note="per layer: route, ids read back, LRU plan on the host, misses copied on a copy stream while "
+             "the resident experts' pass runs, then the filled experts' pass; wall-clock over the timed steps")
+    log(f"[bench] pager: {layer_us:.1f} us/layer, hit rate {rec['hit_rate']}, {rec['h2d_GBps']} GB/s H2D")
+    del pools, host
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -345,6 +446,8 @@ def main():
         L = args.layers or CONFIGS[name].layers
         recs.append(measure(args, name, T, L, args.cpu_seconds if i == 0 else args.cpu_seconds_records,
                             (name, T) in MFMA_BOUND))
+    if not args.config and not args.no_pager:
+        recs.append(measure_pager(args))
     head = recs[0]
     res = {
         "metric": "MoE expert-layer tokens/s (layer tokens per second over the layer stack)",

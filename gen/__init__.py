@@ -10,6 +10,6 @@ from .configs import CONFIGS, Config, config_by_name  # noqa: F401
 from .inputs import (  # noqa: F401
     FMT_FP8_E4M3_ROW, FMT_INT4_G128, slot_layout, slot_bytes, pool_stride,
     ExpertBank, LayerInputs, make_layer, make_bank, bf16_round, bf16_bits_to_f64,
-    layer_pool_bytes, zipf_prior, encode_slot, INT4_GROUP, router_inputs,
+    layer_pool_bytes, zipf_prior, encode_slot, INT4_GROUP, router_inputs, step_tokens,
 )
 from .exact import make_integer_layer, integer_weights, IntegerBank  # noqa: F401

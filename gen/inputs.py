@@ -228,6 +228,20 @@ def router_inputs(cfg: Config, T: int, layer: int):
     return Wg.astype(np.float32), bias.astype(np.float32)
 
 
+def step_tokens(cfg: Config, T: int, layer: int, step: int):
+    """Token rows and router logits of decode step `step` of one layer: new
+    N(0, 1) rows each step (rounded to bf16), the layer's gate and log-Zipf
+    prior fixed across steps (router_inputs), logits = fp32(x W_g^T + bias)
+    computed in fp64. Reuse across steps comes from the prior alone."""
+    c = cfg
+    x = np.random.default_rng(np.random.SeedSequence([c.cfg_id, T, layer, 100, step])).standard_normal(
+        (T, c.H), dtype=np.float32)
+    x_bits = bf16_round(x)
+    Wg, bias = router_inputs(c, T, layer)
+    logits = (bf16_bits_to_f64(x_bits) @ Wg.astype(np.float64).T + bias.astype(np.float64)[None, :]).astype(np.float32)
+    return x_bits, logits
+
+
 def make_layer(cfg: Config, T: int, layer: int) -> LayerInputs:
     c = cfg
     E, H, k = c.E, c.H, c.k

@@ -181,6 +181,59 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
                    int block_m, int act_mode, uint16_t* d_out,
                    void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- resident-first passes
+ * [EP] "hierarchical paging of expert weights": an expert missing from VRAM
+ * is copied in from its host-RAM slot; [MG] section 3: host-to-GPU copies
+ * overlap GPU compute. A block whose block_slot entry is MOE_SLOT_DEFERRED
+ * is left untouched by moe_expert_ffn_pass: its pairs' rows in the
+ * workspace keep their contents (moe_align copies the marker from
+ * slot_of_expert and does not count it as an error). moe_expert_ffn_pass is
+ * moe_expert_ffn with that rule, and with the combine into d_out run only
+ * when last_pass != 0. Two calls on the same stream with the same workspace
+ * and sorted pairs, the first deferring the blocks of experts whose slots are
+ * still being filled and the second deferring every other block (last_pass =
+ * 1), write exactly what one moe_expert_ffn call over the filled pool writes:
+ * each pair's row is computed once, by the same kernels. Workspace
+ * poisoning (moe_debug_poison) does not apply to these calls. */
+#define MOE_SLOT_DEFERRED (-2)
+int moe_expert_ffn_pass(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E,
+                        const float* d_topk_w, const int32_t* d_sorted_pair, const int32_t* d_block_slot,
+                        const int32_t* d_n_padded, int block_m, int act_mode, int last_pass, uint16_t* d_out,
+                        void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- slot-miss path
+ * [EP] "hierarchical paging of expert weights": every MoE layer owns its
+ * VRAM slots, one expert per slot, managed LRU; an expert that is needed and
+ * not in VRAM is copied in from its host-RAM slot. [MG] section 3: the copies
+ * run alongside GPU compute (see moe_expert_ffn_pass).
+ * moe_pager_create: n_layers layers of E experts and n_slots VRAM slots each,
+ * all empty; NULL on bad sizes. moe_pager_plan (host only): for the experts
+ * `needed` (host ids; duplicates and ids outside [0, E) ignored) of one step
+ * of layer `layer`, a resident expert is a hit; each miss, in ascending
+ * expert id, takes the lowest free slot, else the slot of the resident expert
+ * not needed by this step that was used least recently (ties to the lower
+ * id); then every needed expert counts as used by this step. Writes the
+ * layer's table after the step (slot_of_expert, host i32 [E], -1 = not
+ * resident) and the fills (fill_expert, fill_slot: host i32 [>= n_slots],
+ * *n_fill entries). MOE_EINVAL when the step needs more distinct experts than
+ * there are slots (the caller then uses a working buffer that holds them
+ * all). moe_pager_stats: hits and misses so far of one layer (-1: all).
+ * moe_pager_fill: for each fill i, copies h_bank_stride bytes of host row
+ * fill_src[i] of h_bank (page-locked host memory, rows of h_bank_stride <=
+ * slot_bytes bytes) into slot fill_slot[i] of the pool, and the row's format
+ * tag h_bank_fmt[fill_src[i]] (page-locked) into d_slot_fmt[fill_slot[i]],
+ * asynchronously on copy_stream. The caller orders the copies before the
+ * kernels that read those slots (an event), and mirrors the plan's table to
+ * its device slot table. */
+typedef struct moe_pager moe_pager;
+moe_pager* moe_pager_create(int n_layers, int E, int n_slots);
+void moe_pager_destroy(moe_pager* pager);
+int moe_pager_plan(moe_pager* pager, int layer, const int32_t* needed, int n_needed, int32_t* slot_of_expert,
+                   int32_t* fill_expert, int32_t* fill_slot, int* n_fill);
+int moe_pager_stats(const moe_pager* pager, int layer, long long* hits, long long* misses);
+int moe_pager_fill(const moe_slot_pool* pool, const void* h_bank, size_t h_bank_stride, const uint8_t* h_bank_fmt,
+                   const int32_t* fill_src, const int32_t* fill_slot, int n_fill, void* copy_stream);
+
 /* ---------------------------------------------------------------- whole layer
  * The three steps above in one call: the results of moe_route_align followed
  * by moe_expert_ffn on the same stream, every output written as those calls

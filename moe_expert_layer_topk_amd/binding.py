@@ -49,6 +49,14 @@ def _declare(lib):
         "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
         "moe_expert_ffn": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
                                    c_int, c_int, P, P, c_size_t, P]),
+        "moe_pager_create": (c_void_p, [c_int, c_int, c_int]),
+        "moe_pager_destroy": (None, [c_void_p]),
+        "moe_pager_plan": (c_int, [c_void_p, c_int, P, c_int, P, P, P, ctypes.POINTER(c_int)]),
+        "moe_pager_stats": (c_int, [c_void_p, c_int, ctypes.POINTER(ctypes.c_longlong),
+                                    ctypes.POINTER(ctypes.c_longlong)]),
+        "moe_pager_fill": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_size_t, P, P, P, c_int, P]),
+        "moe_expert_ffn_pass": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
+                                        c_int, c_int, c_int, P, P, c_size_t, P]),
         "moe_layer_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
         "moe_layer_noalloc": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, c_int, c_int, c_int, c_int, c_int,
                                       P, P, P, P, P, P, P, P, P, P, P]),
@@ -285,6 +293,74 @@ def expert_ffn(pool, x, k, E, topk_w, aligned, block_m, act_mode, out=None, ws=N
                                 _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
                                 block_m, act_mode, _ptr(out, torch.bfloat16, T * H, "out"),
                                 _ptr(ws, torch.uint8, need, "ws"), c_size_t(ws.numel()), _stream(stream)))
+    return out
+
+
+SLOT_DEFERRED = -2
+
+
+class Pager:
+    """moe_pager: per-layer LRU over VRAM slots (host logic in the library)."""
+
+    def __init__(self, n_layers, E, n_slots):
+        self.E, self.n_slots = E, n_slots
+        self._p = lib().moe_pager_create(n_layers, E, n_slots)
+        if not self._p:
+            raise MoeError("moe_pager_create: bad sizes")
+
+    def __del__(self):
+        if getattr(self, "_p", None):
+            lib().moe_pager_destroy(self._p)
+            self._p = None
+
+    def plan(self, layer, needed):
+        """needed: host int array. Returns (slot_of_expert [E], fill_expert, fill_slot) as numpy int32."""
+        import numpy as np
+        nd = np.ascontiguousarray(needed, dtype=np.int32).reshape(-1)
+        table = np.empty(self.E, dtype=np.int32)
+        fe = np.empty(max(self.n_slots, 1), dtype=np.int32)
+        fs = np.empty(max(self.n_slots, 1), dtype=np.int32)
+        n = c_int(0)
+        _check(lib().moe_pager_plan(self._p, layer, nd.ctypes.data_as(c_void_p), nd.size,
+                                    table.ctypes.data_as(c_void_p), fe.ctypes.data_as(c_void_p),
+                                    fs.ctypes.data_as(c_void_p), ctypes.byref(n)))
+        return table, fe[:n.value].copy(), fs[:n.value].copy()
+
+    def stats(self, layer=-1):
+        h, m = ctypes.c_longlong(0), ctypes.c_longlong(0)
+        _check(lib().moe_pager_stats(self._p, layer, ctypes.byref(h), ctypes.byref(m)))
+        return h.value, m.value
+
+
+def pager_fill(pool, h_bank, h_bank_fmt, fill_src, fill_slot, copy_stream):
+    """moe_pager_fill: h_bank pinned uint8 [rows, stride], h_bank_fmt pinned uint8 [rows];
+    fill_src / fill_slot host int arrays."""
+    import numpy as np
+    src = np.ascontiguousarray(fill_src, dtype=np.int32)
+    dst = np.ascontiguousarray(fill_slot, dtype=np.int32)
+    if not (h_bank.is_pinned() and h_bank_fmt.is_pinned()):
+        raise MoeError("host bank and format tags must be page-locked (pin_memory=True)")
+    _check(lib().moe_pager_fill(pool.c_ref(), c_void_p(h_bank.data_ptr()), h_bank.shape[1],
+                                c_void_p(h_bank_fmt.data_ptr()), src.ctypes.data_as(c_void_p),
+                                dst.ctypes.data_as(c_void_p), int(src.size), c_void_p(copy_stream.cuda_stream)))
+
+
+def expert_ffn_pass(pool, x, k, E, topk_w, aligned, block_m, act_mode, last_pass, out, ws, stream=None):
+    """moe_expert_ffn_pass: blocks whose slot is SLOT_DEFERRED are left alone;
+    the combine into out runs only when last_pass. ws must persist between
+    the passes of one sequence."""
+    import torch
+    T, H = x.shape
+    need = ffn_workspace_bytes(T, k, E, pool.hidden, pool.inter, block_m, act_mode)
+    cap = align_capacity(T, k, E, block_m)
+    _check(lib().moe_expert_ffn_pass(pool.c_ref(), _ptr(x, torch.bfloat16, T * H, "x"), T, k, E,
+                                     _ptr(topk_w, torch.float32, T * k, "topk_w"),
+                                     _ptr(aligned["sorted_pair"], torch.int32, cap, "sorted_pair"),
+                                     _ptr(aligned["block_slot"], torch.int32, cap // block_m, "block_slot"),
+                                     _ptr(aligned["n_padded"], torch.int32, 1, "n_padded"),
+                                     block_m, act_mode, 1 if last_pass else 0,
+                                     _ptr(out, torch.bfloat16, T * H, "out"), _ptr(ws, torch.uint8, need, "ws"),
+                                     c_size_t(ws.numel()), _stream(stream)))
     return out
 
 

@@ -202,9 +202,13 @@ size_t moe_ffn_workspace_bytes(int T, int k, int E, int hidden, int inter, int b
     return 0;
 }
 
-int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E, const float* d_topk_w,
-                   const int32_t* d_sorted_pair, const int32_t* d_block_slot, const int32_t* d_n_padded,
-                   int block_m, int act_mode, uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E, const float* d_topk_w,
+               const int32_t* d_sorted_pair, const int32_t* d_block_slot, const int32_t* d_n_padded, int block_m,
+               int act_mode, uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream, moe::FfnPass pass) {
     moe::PoolArgs pa;
     if (!pool_args(pool, &pa)) return MOE_EINVAL;
     if (!d_x || !d_topk_w || !d_sorted_pair || !d_block_slot || !d_n_padded || !d_out || !d_ws) return MOE_EINVAL;
@@ -216,17 +220,36 @@ int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k,
         if (T > moe::stream_max_tokens()) return MOE_EINVAL;
         if (ws_bytes < moe::stream_workspace_bytes(T, k, pa.hidden, pa.inter, cap)) return MOE_EINVAL;
         clear_stale_error();
-    return hip_status(moe::launch_ffn_stream(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
-                                                 cap, block_m, d_out, d_ws, (hipStream_t)stream));
+        return hip_status(moe::launch_ffn_stream(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
+                                                 cap, block_m, d_out, d_ws, (hipStream_t)stream, pass));
     }
     if (act_mode == MOE_ACT_FP8_G128_POW2) {
         if (block_m != 64 && block_m != 128) return MOE_EINVAL;
         if (ws_bytes < moe::grouped_workspace_bytes(T, k, pa.hidden, pa.inter, cap)) return MOE_EINVAL;
         clear_stale_error();
-    return hip_status(moe::launch_ffn_grouped(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
-                                                  cap, block_m, d_out, d_ws, (hipStream_t)stream));
+        return hip_status(moe::launch_ffn_grouped(pa, d_x, T, k, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded,
+                                                  cap, block_m, d_out, d_ws, (hipStream_t)stream, pass));
     }
     return MOE_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E, const float* d_topk_w,
+                   const int32_t* d_sorted_pair, const int32_t* d_block_slot, const int32_t* d_n_padded,
+                   int block_m, int act_mode, uint16_t* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+    return expert_ffn(pool, d_x, T, k, E, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded, block_m, act_mode, d_out,
+                      d_ws, ws_bytes, stream, moe::FFN_WHOLE);
+}
+
+int moe_expert_ffn_pass(const moe_slot_pool* pool, const uint16_t* d_x, int T, int k, int E, const float* d_topk_w,
+                        const int32_t* d_sorted_pair, const int32_t* d_block_slot, const int32_t* d_n_padded,
+                        int block_m, int act_mode, int last_pass, uint16_t* d_out, void* d_ws, size_t ws_bytes,
+                        void* stream) {
+    return expert_ffn(pool, d_x, T, k, E, d_topk_w, d_sorted_pair, d_block_slot, d_n_padded, block_m, act_mode, d_out,
+                      d_ws, ws_bytes, stream, last_pass ? moe::FFN_PASS_LAST : moe::FFN_PASS);
 }
 
 size_t moe_layer_workspace_bytes(int T, int k, int E, int hidden, int inter, int block_m, int act_mode) {

@@ -78,7 +78,7 @@ __device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_sl, in
         s_sl[e] = sl;
         counts[e] = c;
         seg_offset[e] = off;
-        if (sl < 0 && c > 0) atomicAdd(err, c);
+        if (sl < 0 && sl != MOE_SLOT_DEFERRED && c > 0) atomicAdd(err, c);   // (deferred: not an error)
     }
     if (e == 0) {
         seg_offset[E] = total;

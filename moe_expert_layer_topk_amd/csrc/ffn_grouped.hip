@@ -380,6 +380,7 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
     const int n0 = nt_idx * 128;
     if (int4_only && slot >= 0 && pool.fmt[slot] != 1) return;   // FP8: elsewhere
     if (slot < 0) {                                   // unusable slot (e.g. not resident): its pairs add zero
+        if (block_slot[mt_idx] == MOE_SLOT_DEFERRED) return;   // (a deferred block's rows are left as they are)
         for (int i = threadIdx.x; i < BM * 16; i += GT) {
             int r = i >> 4, ch = i & 15;
             int p = sorted_pair[mt_idx * BM + r];
@@ -596,7 +597,7 @@ template <int BM>
 static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const GroupedWs& w, const uint16_t* x, int T, int k,
                                     const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
                                     const int32_t* n_padded, int cap, int H, int I, uint16_t* out,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, FfnPass pass) {
     const int NP = T * k;
     const long qitems = (long)T * (H / MOE_ACT_G);      // 16 per block
     MOE_LAUNCH(K_QUANT_ACT, stream, quant_act_kernel, dim3((unsigned)((qitems + 15) / 16)), dim3(256), 0, stream, x, T, H,
@@ -630,12 +631,13 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (pass == FFN_PASS) return hipSuccess;          // rows only: a later pass combines
     return launch_combine_bf16(w.ybuf, topk_w, T, k, H, out, stream);
 }
 
 hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                               const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
-                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream) {
+                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream, FfnPass pass) {
     GPool gp;
     gp.base = (const uint8_t*)pa.base;
     gp.stride = pa.stride;
@@ -645,16 +647,16 @@ hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int 
     gp.n_slots = pa.n_slots;
     gp.fmt_ok = pa.fmt_ok;
     GroupedWs w = grouped_ws_layout(ws, T, k, pa.hidden, pa.inter, cap);
-    if (debug_poison_on()) {                          // activation codes, h and y rows: NaN until written
+    if (pass == FFN_WHOLE && debug_poison_on()) {     // activation codes, h and y rows: NaN until written
         hipError_t e = launch_poison(ws, (size_t)((uint8_t*)w.mm - (uint8_t*)ws), stream);
         if (e != hipSuccess) return e;
     }
     if (block_m == 64)
         return launch_grouped_bm<64>(pa, gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
-                                     pa.inter, out, stream);
+                                     pa.inter, out, stream, pass);
     if (block_m == 128)
         return launch_grouped_bm<128>(pa, gp, w, x, T, k, topk_w, sorted_pair, block_slot, n_padded, cap, pa.hidden,
-                                      pa.inter, out, stream);
+                                      pa.inter, out, stream, pass);
     return hipErrorInvalidValue;
 }
 

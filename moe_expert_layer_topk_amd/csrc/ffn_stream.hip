@@ -837,6 +837,7 @@ __global__ void __launch_bounds__(G_THREADS) gemm2_stream_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pv[nt] = pr[nt] < NP;
     if (slot < 0) {                                   // non-resident expert: its pairs add zero
+        if (slot_in == MOE_SLOT_DEFERRED) return;     // (a deferred block's rows are left as they are)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             if (pv[nt]) *(f32x4*)(ybuf + (size_t)pr[nt] * H + n0 + 4 * q) = f32x4{0, 0, 0, 0};
@@ -1110,8 +1111,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         p2_landed(Wc);
         float* yrow = ybuf + (size_t)(valid ? pr : 0) * H + n0 + 4 * q;
         if (slot < 0) {                               // non-resident expert: its pairs add zero
-            if (valid) *(f32x4*)yrow = f32x4{0, 0, 0, 0};
-            return;
+            if (valid && s_slot[bb] != MOE_SLOT_DEFERRED) *(f32x4*)yrow = f32x4{0, 0, 0, 0};
+            return;                                   // (a deferred block's rows are left as they are)
         }
         f32x4 acc = {0, 0, 0, 0};
         if (fmt == 0) {
@@ -1331,7 +1332,7 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
 
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                              const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
-                             int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream) {
+                             int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream, FfnPass pass) {
     SlotView sv;
     sv.base = (const uint8_t*)pa.base;
     sv.stride = pa.stride;
@@ -1343,7 +1344,7 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
     const int H = pa.hidden, I = pa.inter;
     uint16_t* hbuf = (uint16_t*)ws;
     float* ybuf = (float*)((uint8_t*)ws + up256((size_t)cap * I * sizeof(uint16_t)));
-    if (debug_poison_on()) {                          // h and y rows: NaN until written
+    if (pass == FFN_WHOLE && debug_poison_on()) {     // h and y rows: NaN until written
         hipError_t e = launch_poison(ws, stream_workspace_bytes(T, k, H, I, cap), stream);
         if (e != hipSuccess) return e;
     }
@@ -1355,6 +1356,7 @@ hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (pass == FFN_PASS) return hipSuccess;          // rows only: a later pass combines
     return launch_combine_f32(ybuf, topk_w, T, k, H, out, stream);
 }
 

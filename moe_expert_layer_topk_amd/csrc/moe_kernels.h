@@ -70,9 +70,13 @@ hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int
                               hipStream_t stream);
 hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
                                hipStream_t stream);
+// FFN call kinds: a whole call (workspace poisoning allowed, combine), or one
+// pass of a deferred-block sequence (no poisoning; combine on the last pass)
+enum FfnPass { FFN_WHOLE = 0, FFN_PASS = 1, FFN_PASS_LAST = 2 };
 hipError_t launch_ffn_stream(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                              const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
-                             int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream);
+                             int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream,
+                             FfnPass pass = FFN_WHOLE);
 // whole decode layer (route and align inside the gate/up kernel); layer_stream_ok says where it applies
 bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap);
 size_t layer_stream_workspace_bytes(int T, int k, int H, int I, int cap);
@@ -85,7 +89,8 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
 size_t grouped_workspace_bytes(int T, int k, int H, int I, int cap);
 hipError_t launch_ffn_grouped(const PoolArgs& pa, const uint16_t* x, int T, int k, const float* topk_w,
                               const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
-                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream);
+                              int cap, int block_m, uint16_t* out, void* ws, hipStream_t stream,
+                              FfnPass pass = FFN_WHOLE);
 
 bool mfma_path_ok(int H, int I);
 size_t mfma_ws_bytes(int H, int cap);

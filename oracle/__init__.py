@@ -35,3 +35,4 @@ from .ffn import expert_ffn, ACT_BF16, ACT_FP8_G128_POW2  # noqa: F401
 from .layer import layer_forward  # noqa: F401
 from .router import router_logits, fp32_sum_bound  # noqa: F401
 from .requant import bitwidth_plan, requant_slot  # noqa: F401
+from .pager import LRUSlots  # noqa: F401

@@ -45,6 +45,10 @@ MUTANTS = {
     "requant_zero_sign": ("requant.py", "np.rint((-mn) / s32)", "np.rint(mn / s32)"),
     "requant_nibble_order": ("requant.py", "(q[:, 0::2] | (q[:, 1::2] << 4))", "(q[:, 1::2] | (q[:, 0::2] << 4))"),
     "plan_ties_to_higher_id": ("requant.py", "key=lambda e: (int(counts[e]), e)", "key=lambda e: (int(counts[e]), -e)"),
+    "lru_evicts_most_recent": ("pager.py", "key=lambda v: (self.last[v], v))", "key=lambda v: (-self.last[v], v))"),
+    "lru_free_slot_highest": ("pager.py", "slot = free[0]", "slot = free[-1]"),
+    "lru_no_touch_on_hit": ("pager.py", "        for e in want:\n            self.last[e] = self.step",
+                            "        for e, _ in fills:\n            self.last[e] = self.step"),
 }
 
 
@@ -196,8 +200,19 @@ def pin_requant(m):
     return True
 
 
+def pin_pager(m):
+    import test_oracle_pager as tp
+    saved = tp.oracle
+    tp.oracle = m
+    try:
+        tp.test_lru_hand_case()
+    finally:
+        tp.oracle = saved
+    return True
+
+
 PINS = [pin_e4m3, pin_route, pin_align, pin_ffn, pin_slots, pin_act_quant, pin_dense_C0, pin_router,
-        pin_integer_layer, pin_requant]
+        pin_integer_layer, pin_requant, pin_pager]
 
 
 def all_pins_pass(m):
