@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--calls", choices=("layer", "split"), default="layer",
                     help="layer: one moe_layer call per layer; split: moe_route_align then moe_expert_ffn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-pager", action="store_true", help="leave out the slot-miss path record")
+    ap.add_argument("--no-pager", action="store_true", help="leave out the slot-miss path records")
+    ap.add_argument("--pager-only", action="store_true", help="only the slot-miss path records")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget of the headline workload")
     ap.add_argument("--cpu-seconds-records", type=float, default=5.0, help="... of each other record")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -317,13 +318,16 @@ def measure(args, name, T, L, cpu_seconds, mfma_bound):
     return rec
 
 
-def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
+def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102, packed=False):
     """The slot-miss path over a decode loop: each layer's VRAM pool holds
     n_slots experts, every expert sits in page-locked host RAM, each step
     brings new tokens (the layer's gate and reuse prior fixed). Per layer and
     step: route, read the ids back, plan with the pager, fill the misses on a
     copy stream while the resident experts' pass runs, then the filled
-    experts' pass. Step 0 starts from empty pools; the timed steps are 1..."""
+    experts' pass. Step 0 starts from empty pools; the timed steps are 1...
+    packed: the host bank holds the slots packed (per-row Huffman codes of
+    the FP8 exponents); each fill copies the packed bytes to a staging buffer
+    and expands them into the slot on the copy stream."""
     import torch
     import moe_expert_layer_topk_amd as moe
     from gen import CONFIGS, make_bank, step_tokens
@@ -335,6 +339,13 @@ def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
     bank = make_bank(cfg)
     host = torch.from_numpy(bank.materialize(0)).pin_memory()
     host_fmt = torch.zeros(E, dtype=torch.uint8).pin_memory()
+    if packed:
+        pk = [moe.fp8_pack(host[e].numpy(), H, I) for e in range(E)]
+        p_sizes = np.array([p.size for p in pk], dtype=np.uint64)
+        p_offsets = np.concatenate([[0], np.cumsum(p_sizes)[:-1]]).astype(np.uint64)
+        host_packed = torch.from_numpy(np.concatenate(pk)).pin_memory()
+        staging = torch.empty(int(n_slots * (int(p_sizes.max()) + 16)), dtype=torch.uint8, device=dev)
+        pack_ratio = float(p_sizes.sum()) / (E * bank.stride)
     pools = [moe.SlotPool(torch.zeros((n_slots, bank.stride), dtype=torch.uint8, device=dev),
                           torch.zeros(n_slots, dtype=torch.uint8, device=dev), H, I) for _ in range(L)]
     inputs = []
@@ -358,7 +369,7 @@ def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
     torch.cuda.set_stream(comp)
     torch.cuda.synchronize()
     log(f"[bench] pager {name} T={T} layers={L} slots={n_slots}: inputs ready in {time.time() - t0:.1f}s")
-    stats = dict(bytes=0, fill_ms=0.0, misses=0, hits=0)
+    stats = dict(bytes=0, slot_bytes=0, fill_ms=0.0, misses=0, hits=0)
 
     def run_step(st, timed):
         for l in range(L):
@@ -374,7 +385,10 @@ def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
             copy.wait_stream(comp)                       # earlier kernels may still read the victim slots
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             c0.record(copy)
-            moe.pager_fill(pools[l], host, host_fmt, fe, fs, copy)
+            if packed:
+                moe.pager_fill_packed(pools[l], host_packed, p_offsets, p_sizes, fe, fs, staging, copy)
+            else:
+                moe.pager_fill(pools[l], host, host_fmt, fe, fs, copy)
             c1.record(copy)
             t1d.copy_(t1h, non_blocking=True)
             t2d.copy_(t2h, non_blocking=True)
@@ -386,8 +400,9 @@ def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
             if timed:
                 c1.synchronize()
                 stats["fill_ms"] += c0.elapsed_time(c1)
-                stats["bytes"] += int(fe.size) * bank.stride
+                stats["bytes"] += int(p_sizes[fe].sum()) if packed else int(fe.size) * bank.stride
                 stats["misses"] += int(fe.size)
+                stats["slot_bytes"] += int(fe.size) * bank.stride
                 stats["hits"] += int(len(set(ids_h.numpy().reshape(-1).tolist())) - fe.size)
 
     run_step(0, False)                                   # cold pools
@@ -401,17 +416,22 @@ def measure_pager(args, name="C1", T=8, L=40, steps=8, n_slots=102):
     layer_us = wall / n * 1e6
     rec = dict(
         workload=f"{name} slot-miss path: T={T} tokens x {L} layers, {n_slots} VRAM slots per layer, all {E} experts "
-                 f"in page-locked host RAM, new tokens every step",
+                 f"in page-locked host RAM{' packed (per-row Huffman-coded FP8 exponents)' if packed else ''}, "
+                 f"new tokens every step",
         value=round(T * n / wall, 1), tokens_per_layer=T, layers=L, steps_timed=steps - 1, vram_slots=n_slots,
         layer_us=round(layer_us, 2), hit_rate=round(stats["hits"] / max(1, stats["hits"] + stats["misses"]), 4),
         misses_per_layer_step=round(stats["misses"] / n, 2),
         h2d_GBps=round(stats["bytes"] / max(1e-9, stats["fill_ms"] / 1e3) / 1e9, 2),
         h2d_bytes_per_layer_step=int(stats["bytes"] / n),
+        slot_GBps_delivered=round(stats["slot_bytes"] / max(1e-9, stats["fill_ms"] / 1e3) / 1e9, 2),
         fill_us_per_layer_step=round(stats["fill_ms"] / n * 1e3, 2),
+        host_bank_ratio=round(pack_ratio, 4) if packed else 1.0,
         note="per layer: route, ids read back, LRU plan on the host, misses copied on a copy stream while "
              "the resident experts' pass runs, then the filled experts' pass; wall-clock over the timed steps")
     log(f"[bench] pager: {layer_us:.1f} us/layer, hit rate {rec['hit_rate']}, {rec['h2d_GBps']} GB/s H2D")
     del pools, host
+    if packed:
+        del staging, host_packed
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec
@@ -435,6 +455,9 @@ def main():
         return
     from gen import CONFIGS
 
+    if args.pager_only:
+        print(json.dumps({"records": [measure_pager(args), measure_pager(args, packed=True)]}), flush=True)
+        return
     if args.config:
         cfg = CONFIGS[args.config]
         T = args.tokens or (max(t for t in cfg.Ts if t <= 64) if min(cfg.Ts) <= 64 else cfg.Ts[0])
@@ -448,6 +471,7 @@ def main():
                             (name, T) in MFMA_BOUND))
     if not args.config and not args.no_pager:
         recs.append(measure_pager(args))
+        recs.append(measure_pager(args, packed=True))
     head = recs[0]
     res = {
         "metric": "MoE expert-layer tokens/s (layer tokens per second over the layer stack)",

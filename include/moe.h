@@ -234,6 +234,43 @@ int moe_pager_stats(const moe_pager* pager, int layer, long long* hits, long lon
 int moe_pager_fill(const moe_slot_pool* pool, const void* h_bank, size_t h_bank_stride, const uint8_t* h_bank_fmt,
                    const int32_t* fill_src, const int32_t* fill_slot, int n_fill, void* copy_stream);
 
+/* ---------------------------------------------------------------- compressed host tier
+ * [EP] weight-compression section: FP8 exponents are skewed, so the exponent
+ * bits of each row of an expert's matrices are Huffman-coded in host RAM and
+ * expanded on the GPU right after the copy into VRAM.
+ * Packed slot (every part on a 16-byte boundary): eight u32 (0x38504D46,
+ * hidden, inter, offset and size of packed w13, offset and size of packed
+ * w2, total size), packed w13 [2I rows x H], w13 row scales f32 [2I], packed
+ * w2 [H rows x I], w2 row scales f32 [H]. Packed matrix of R rows x C
+ * values (C a multiple of 256): code lengths u8 [R][8] (symbol 2i in the low
+ * nibble of byte i), chunk start bits u32 [R][C/256] (bit offsets into the
+ * matrix stream), sign|mantissa nibbles u8 [R][C/2] (value c in the low
+ * nibble of byte c/2 when c is even), the exponent stream (least significant
+ * bit of each byte first), 8 zero bytes. An e4m3 byte is sign | exponent (4
+ * bits) | mantissa (3); the exponent is coded. Each row's code is canonical
+ * (symbols by (length, symbol) take consecutive codes, written first bit
+ * first) with Huffman lengths from the row's exponent counts (merge the two
+ * lightest nodes, ties to the node holding the lower symbol; one symbol
+ * present: length 1); while a length exceeds 8 the counts of the present
+ * symbols are raised by floor(total * 2^k / 256) + 1, k = 0, 1, ... hidden
+ * and inter must be multiples of 256.
+ * moe_fp8_pack (host only): packs the FP8 slot at h_fp8_slot into h_out
+ * (capacity cap >= moe_fp8_pack_bound); returns the packed size (0 = bad
+ * arguments). moe_fp8_unpack: expands the packed slot at d_packed (device)
+ * into FP8 slot dst_slot and sets its tag to MOE_FMT_FP8_E4M3_ROW; a header
+ * that does not match the pool writes nothing and adds 1 to d_err (may be
+ * NULL). moe_pager_fill_packed: moe_pager_fill from a host bank of packed
+ * slots (row r at h_packed + h_offsets[r], h_sizes[r] bytes, page-locked):
+ * each fill is copied into the device staging buffer (the fills' sizes, each
+ * rounded up to 16, must fit staging_bytes) and expanded into its slot, all
+ * on copy_stream. */
+size_t moe_fp8_pack_bound(int hidden, int inter);
+size_t moe_fp8_pack(const uint8_t* h_fp8_slot, int hidden, int inter, uint8_t* h_out, size_t cap);
+int moe_fp8_unpack(const moe_slot_pool* pool, const uint8_t* d_packed, int dst_slot, int32_t* d_err, void* stream);
+int moe_pager_fill_packed(const moe_slot_pool* pool, const uint8_t* h_packed, const uint64_t* h_offsets,
+                          const uint64_t* h_sizes, const int32_t* fill_src, const int32_t* fill_slot, int n_fill,
+                          uint8_t* d_staging, size_t staging_bytes, int32_t* d_err, void* copy_stream);
+
 /* ---------------------------------------------------------------- whole layer
  * The three steps above in one call: the results of moe_route_align followed
  * by moe_expert_ffn on the same stream, every output written as those calls

@@ -55,6 +55,10 @@ def _declare(lib):
         "moe_pager_stats": (c_int, [c_void_p, c_int, ctypes.POINTER(ctypes.c_longlong),
                                     ctypes.POINTER(ctypes.c_longlong)]),
         "moe_pager_fill": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_size_t, P, P, P, c_int, P]),
+        "moe_fp8_pack_bound": (c_size_t, [c_int, c_int]),
+        "moe_fp8_pack": (c_size_t, [P, c_int, c_int, P, c_size_t]),
+        "moe_fp8_unpack": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, P, P]),
+        "moe_pager_fill_packed": (c_int, [ctypes.POINTER(moe_slot_pool), P, P, P, P, P, c_int, P, c_size_t, P, P]),
         "moe_expert_ffn_pass": (c_int, [ctypes.POINTER(moe_slot_pool), P, c_int, c_int, c_int, P, P, P, P,
                                         c_int, c_int, c_int, P, P, c_size_t, P]),
         "moe_layer_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
@@ -330,6 +334,44 @@ class Pager:
         h, m = ctypes.c_longlong(0), ctypes.c_longlong(0)
         _check(lib().moe_pager_stats(self._p, layer, ctypes.byref(h), ctypes.byref(m)))
         return h.value, m.value
+
+
+def fp8_pack(slot_bytes_u8, hidden, inter):
+    """moe_fp8_pack on a host numpy FP8 slot -> packed numpy uint8."""
+    import numpy as np
+    src = np.ascontiguousarray(slot_bytes_u8, dtype=np.uint8)
+    cap = int(lib().moe_fp8_pack_bound(hidden, inter))
+    if cap == 0:
+        raise MoeError("moe_fp8_pack: hidden and inter must be multiples of 256")
+    out = np.empty(cap, dtype=np.uint8)
+    n = int(lib().moe_fp8_pack(src.ctypes.data_as(c_void_p), hidden, inter, out.ctypes.data_as(c_void_p), cap))
+    if n == 0:
+        raise MoeError("moe_fp8_pack failed")
+    return out[:n].copy()
+
+
+def fp8_unpack(pool, packed_dev, dst_slot, err=None, stream=None):
+    import torch
+    _check(lib().moe_fp8_unpack(pool.c_ref(), _ptr(packed_dev, torch.uint8, 32, "packed"), int(dst_slot),
+                                _ptr(err, torch.int32, 1, "err") if err is not None else None, _stream(stream)))
+
+
+def pager_fill_packed(pool, h_packed, offsets, sizes, fill_src, fill_slot, staging, copy_stream, err=None):
+    """moe_pager_fill_packed: h_packed pinned uint8 (all packed rows back to back),
+    offsets / sizes numpy uint64 per bank row; staging a device uint8 buffer."""
+    import numpy as np
+    import torch
+    if not h_packed.is_pinned():
+        raise MoeError("the packed host bank must be page-locked (pin_memory=True)")
+    off = np.ascontiguousarray(offsets, dtype=np.uint64)
+    siz = np.ascontiguousarray(sizes, dtype=np.uint64)
+    src = np.ascontiguousarray(fill_src, dtype=np.int32)
+    dst = np.ascontiguousarray(fill_slot, dtype=np.int32)
+    _check(lib().moe_pager_fill_packed(pool.c_ref(), c_void_p(h_packed.data_ptr()), off.ctypes.data_as(c_void_p),
+                                       siz.ctypes.data_as(c_void_p), src.ctypes.data_as(c_void_p),
+                                       dst.ctypes.data_as(c_void_p), int(src.size), _ptr(staging, torch.uint8),
+                                       staging.numel(), _ptr(err, torch.int32, 1, "err") if err is not None else None,
+                                       c_void_p(copy_stream.cuda_stream)))
 
 
 def pager_fill(pool, h_bank, h_bank_fmt, fill_src, fill_slot, copy_stream):

@@ -12,7 +12,7 @@ int record_hip_error(int hip_error);
 
 // kernel ids for launch tracing (names in profile.hip)
 enum KernelId { K_ROUTE, K_ROUTE_ALIGN, K_ALIGN_SINGLE, K_ALIGN_HIST, K_ALIGN_SCAN, K_ALIGN_SCATTER, K_GEMM1_STREAM,
-                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_POOL_CHECK, K_POISON, K_ROUTER_GEMM, K_REQUANT, K_COUNT };
+                K_GEMM2_STREAM, K_QUANT_ACT, K_GEMM1_FP8, K_GEMM2_FP8, K_GEMM1_TILE, K_GEMM2_TILE, K_MFMA_PREP, K_COMBINE, K_DEQUANT, K_POOL_CHECK, K_POISON, K_ROUTER_GEMM, K_REQUANT, K_UNPACK, K_COUNT };
 // events the next launch of kernel `kid` on `s` should stamp (false: not tracing)
 bool prof_events(int kid, hipStream_t s, hipEvent_t* start, hipEvent_t* stop);
 

@@ -23,7 +23,7 @@ std::vector<hipEvent_t> g_free;
 const char* kNames[K_COUNT] = {"route", "route_align", "align_single", "align_hist", "align_scan", "align_scatter",
                                "gemm1_stream", "gemm2_stream", "quant_act", "gemm1_fp8", "gemm2_fp8", "gemm1_tile", "gemm2_tile", "mfma_prep",
                                "combine", "dequant", "pool_check", "poison", "router_gemm",
-                               "requant"};
+                               "requant", "fp8_unpack"};
 
 hipEvent_t take_event() {
     if (!g_free.empty()) {

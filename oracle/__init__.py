@@ -36,3 +36,4 @@ from .layer import layer_forward  # noqa: F401
 from .router import router_logits, fp32_sum_bound  # noqa: F401
 from .requant import bitwidth_plan, requant_slot  # noqa: F401
 from .pager import LRUSlots  # noqa: F401
+from . import huffman  # noqa: F401

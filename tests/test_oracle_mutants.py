@@ -47,6 +47,12 @@ MUTANTS = {
     "plan_ties_to_higher_id": ("requant.py", "key=lambda e: (int(counts[e]), e)", "key=lambda e: (int(counts[e]), -e)"),
     "lru_evicts_most_recent": ("pager.py", "key=lambda v: (self.last[v], v))", "key=lambda v: (-self.last[v], v))"),
     "lru_free_slot_highest": ("pager.py", "slot = free[0]", "slot = free[-1]"),
+    "huffman_ties_to_higher_symbol": ("huffman.py", "nodes.sort(key=lambda n: (n[0], n[1]))",
+                                      "nodes.sort(key=lambda n: (n[0], -n[1]))"),
+    "huffman_no_length_limit": ("huffman.py", "while max(lens) > MAX_LEN:", "while max(lens) > MAX_LEN + 8:"),
+    "huffman_floor_not_scaled": ("huffman.py", "floor = (total << k) // 256 + 1", "floor = total // 256 + 1 + k"),
+    "huffman_canonical_order": ("huffman.py", "order = sorted((l, s) for s, l in enumerate(lens) if l > 0)",
+                                "order = sorted((l, -s) for s, l in enumerate(lens) if l > 0)\n    order = [(l, -s) for l, s in order]"),
     "lru_no_touch_on_hit": ("pager.py", "        for e in want:\n            self.last[e] = self.step",
                             "        for e, _ in fills:\n            self.last[e] = self.step"),
 }
@@ -211,8 +217,24 @@ def pin_pager(m):
     return True
 
 
+def pin_huffman(m):
+    import test_oracle_huffman as th
+    saved = th.huffman
+    th.huffman = m.huffman
+    try:
+        th.test_textbook_huffman_lengths()
+        th.test_ties_single_symbol_and_flat_fallback()
+        # canonical code values of a fixed set of lengths, worked by hand
+        codes = m.huffman.canonical_codes([2, 0, 3, 3, 2, 2] + [0] * 10)
+        if codes != {0: (0, 2), 4: (1, 2), 5: (2, 2), 2: (6, 3), 3: (7, 3)}:
+            return False
+    finally:
+        th.huffman = saved
+    return True
+
+
 PINS = [pin_e4m3, pin_route, pin_align, pin_ffn, pin_slots, pin_act_quant, pin_dense_C0, pin_router,
-        pin_integer_layer, pin_requant, pin_pager]
+        pin_integer_layer, pin_requant, pin_pager, pin_huffman]
 
 
 def all_pins_pass(m):
