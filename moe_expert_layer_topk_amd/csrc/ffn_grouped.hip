@@ -97,40 +97,6 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 packed int4 codes (8 bytes, low nibble first) -> 16 e4m3 codes of
-// q - zero, in K order (exact for integer zero points: q - zero is an integer
-// in [-15, 15]). Each pair of nibbles becomes two fp16 values 1024 + q (the
-// exponent of 1024 with q in the low mantissa bits), minus 1024 + zero, then
-// two e4m3 codes; four vector instructions per pair.
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void int4_to_e4m3_16(uint2 packed, float zero, uint32_t out[4]) {
-    const _Float16 zz = (_Float16)(-1024.0f - zero);
-    const f16x2_t off = {zz, zz};
-    const uint32_t w[2] = {packed.x, packed.y};
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        const uint32_t ev = w[d] & 0x0F0F0F0Fu;              // nibbles 0, 2, 4, 6 as bytes
-        const uint32_t od = (w[d] >> 4) & 0x0F0F0F0Fu;       // nibbles 1, 3, 5, 7
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {                         // output dword: nibble pairs 2h, 2h + 1
-            f16x2_t v[2];
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                const int p = 2 * h + pp;
-                // bytes: ev.p, 0, od.p, 0 (perm selector 12 gives a zero byte)
-                const uint32_t sel = (uint32_t)p | (12u << 8) | ((uint32_t)(4 + p) << 16) | (12u << 24);
-                const uint32_t bits = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
-                v[pp] = __builtin_bit_cast(f16x2_t, bits) + off;
-            }
-            s16x2_t acc = {0, 0};
-            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(acc, v[0], 1.0f, false);   // low word
-            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(acc, v[1], 1.0f, true);    // high word
-            out[2 * d + h] = __builtin_bit_cast(uint32_t, acc);
-        }
-    }
-}
-
 // ------------------------------------------------------------ gemm1
 // Tile: BM pair rows x 128 inter columns (128 gate rows + 128 up rows of W13).
 // Wave w owns inter columns [32w, 32w+32).
@@ -616,13 +582,29 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 0, stream);
         if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, dim3(g1.x, oy), dim3(GT), sm1, stream, gp, w.xq, w.xs,
-                   NP, k, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1, olist, n_olist);
+        const int32_t* tokrow = nullptr;
+        const float* wsort = nullptr;
+        const uint8_t* scl = nullptr;
+        mfma_prep_arrays(w.mm, cap, &tokrow, &wsort, &scl);
+        if (int4_ring_ok(H, I)) {
+            e = launch_gemm1_int4_ring(pa, w.xq, tokrow, scl, block_slot, I, w.hq, w.hs, olist, n_olist, oy, stream);
+            if (e != hipSuccess) return e;
+        } else {
+            MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, dim3(g1.x, oy), dim3(GT), sm1, stream, gp, w.xq,
+                       w.xs, NP, k, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1, olist, n_olist);
+        }
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 1, stream);
         if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, dim3(g2.x, oy), dim3(GT), gemm2_smem<BM>(), stream, gp,
-                   NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1, olist, n_olist);
+        if (int4_ring_ok(H, I)) {
+            e = launch_gemm2_int4_ring(pa, NP, wsort, sorted_pair, block_slot, I, w.hq, w.hs, w.ybuf, olist, n_olist,
+                                       oy, stream);
+            if (e != hipSuccess) return e;
+        } else {
+            MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, dim3(g2.x, oy), dim3(GT), gemm2_smem<BM>(), stream,
+                       gp, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1, olist,
+                       n_olist);
+        }
     } else {
         MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
                    sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 0, nullptr, nullptr);

@@ -590,6 +590,14 @@ void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_l
     *list = (const int*)(p + 256);
 }
 
+void mfma_prep_arrays(void* ws, int cap, const int32_t** tokrow, const float** wsort, const uint8_t** scl) {
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    const uint8_t* p = (const uint8_t*)ws + up((size_t)(cap / MM_BM) * 16) + 256 + up((size_t)(cap / MM_BM) * 4);
+    *tokrow = (const int32_t*)p;
+    *wsort = (const float*)(p + up((size_t)cap * 4));
+    *scl = p + 2 * up((size_t)cap * 4);
+}
+
 hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
                            const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
                            const int32_t* n_padded, int cap, uint8_t* hq, uint8_t* hs, uint16_t* ybuf, void* ws,

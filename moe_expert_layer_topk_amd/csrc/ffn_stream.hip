@@ -24,6 +24,8 @@
 // which leaves the contraction unchanged.
 #include "moe_common.h"
 #include "moe_kernels.h"
+
+#include <atomic>
 #include "route_dev.h"
 
 namespace moe {
@@ -1260,15 +1262,18 @@ int stream_max_tokens() { return STREAM_MAX_T; }
 
 // compute units of the current device (cached per device id)
 int device_cus() {
-    static int cached[64] = {0};
+    // per device, filled once; racing callers store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
+        c = n;
     }
-    return cached[dev];
+    return c;
 }
 
 static size_t up256(size_t n) { return (n + 255) / 256 * 256; }

@@ -155,4 +155,55 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8&
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// 16 packed int4 codes (8 bytes, low nibble first) -> 16 e4m3 codes of
+// q - zero, in K order (exact for integer zero points: q - zero is an integer
+// in [-15, 15]). Each pair of nibbles becomes two fp16 values 1024 + q (the
+// exponent of 1024 with q in the low mantissa bits), minus 1024 + zero, then
+// two e4m3 codes; four vector instructions per pair.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void int4_to_e4m3_16(uint2 packed, float zero, uint32_t out[4]) {
+    const _Float16 zz = (_Float16)(-1024.0f - zero);
+    const f16x2_t off = {zz, zz};
+    const uint32_t w[2] = {packed.x, packed.y};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const uint32_t ev = w[d] & 0x0F0F0F0Fu;              // nibbles 0, 2, 4, 6 as bytes
+        const uint32_t od = (w[d] >> 4) & 0x0F0F0F0Fu;       // nibbles 1, 3, 5, 7
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                         // output dword: nibble pairs 2h, 2h + 1
+            f16x2_t v[2];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int p = 2 * h + pp;
+                // bytes: ev.p, 0, od.p, 0 (perm selector 12 gives a zero byte)
+                const uint32_t sel = (uint32_t)p | (12u << 8) | ((uint32_t)(4 + p) << 16) | (12u << 24);
+                const uint32_t bits = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
+                v[pp] = __builtin_bit_cast(f16x2_t, bits) + off;
+            }
+            s16x2_t acc = {0, 0};
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(acc, v[0], 1.0f, false);   // low word
+            acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(acc, v[1], 1.0f, true);    // high word
+            out[2 * d + h] = __builtin_bit_cast(uint32_t, acc);
+        }
+    }
+}
+
+// Direct-to-LDS loads: lane i writes 16 (4) bytes at lds + 16 i (4 i); lds is
+// wave-uniform. They count on the vector memory counter like other loads.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt left open): at most N
+// of this wave's vector memory operations stay outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace moe

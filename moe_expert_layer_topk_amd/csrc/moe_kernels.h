@@ -96,6 +96,9 @@ bool mfma_path_ok(int H, int I);
 size_t mfma_ws_bytes(int H, int cap);
 // blocks the prep kernel found int4 or not resident (device list and count)
 void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_list);
+// per sorted position, written by the prep kernel: token (0 for padding),
+// route weight (0 for padding), activation exponent bytes [block][K step][128 rows]
+void mfma_prep_arrays(void* ws, int cap, const int32_t** tokrow, const float** wsort, const uint8_t** scl);
 // phase 0: prep + gate/up kernel, phase 1: down kernel
 hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t* xs, int NP, int k,
                            const float* topk_w, const int32_t* sorted_pair, const int32_t* block_slot,
@@ -118,5 +121,17 @@ hipError_t launch_requant(const PoolArgs& pa, int src, int dst, uint8_t* tags, i
 void set_debug_poison(int on);
 bool debug_poison_on();
 hipError_t launch_poison(void* p, size_t bytes, hipStream_t stream);
+
+// int4 blocks listed beside the FP8 matrix-core kernels, gate/up GEMM on an
+// LDS ring (H and I multiples of 128 up to 2048)
+bool int4_ring_ok(int H, int I);
+hipError_t launch_gemm1_int4_ring(const PoolArgs& pa, const uint8_t* xq, const int32_t* tokrow, const uint8_t* scl,
+                                  const int32_t* block_slot, int I, uint8_t* hq, uint8_t* hs, const int* list,
+                                  const int* n_list, int grid_y, hipStream_t stream);
+// ... and the down GEMM (with zero rows for listed blocks whose slot is not usable)
+hipError_t launch_gemm2_int4_ring(const PoolArgs& pa, int NP, const float* wsort, const int32_t* sorted_pair,
+                                  const int32_t* block_slot, int I, const uint8_t* hq, const uint8_t* hs,
+                                  uint16_t* ybuf, const int* list, const int* n_list, int grid_y,
+                                  hipStream_t stream);
 
 }  // namespace moe
