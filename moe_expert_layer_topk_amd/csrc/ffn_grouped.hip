@@ -100,13 +100,13 @@ __device__ __forceinline__ void barrier_lds() {
 // ------------------------------------------------------------ gemm1
 // Tile: BM pair rows x 128 inter columns (128 gate rows + 128 up rows of W13).
 // Wave w owns inter columns [32w, 32w+32).
-template <int BM, bool ONLY4>
+template <int BM>
 __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __restrict__ xq,
                                            const uint8_t* __restrict__ xs, int NP, int k,
                                            const int32_t* __restrict__ sorted_pair,
                                            const int32_t* __restrict__ block_slot,
                                            const int32_t* __restrict__ n_padded, int H, int I,
-                                           uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, int int4_only,
+                                           uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
                                            const int mt_idx, const int nt_idx) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -123,8 +123,7 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
     if (slot < 0) return;
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
     const int fmt_slot = pool.fmt[slot];
-    if (int4_only && fmt_slot == 0) return;
-    const int fmt = ONLY4 ? 1 : fmt_slot;             // (the int4-only instance has no FP8 path)
+    const int fmt = fmt_slot;
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int c0 = nt_idx * 128;                      // first inter column of the tile
     const int ncols = min(128, I - c0);               // valid inter columns
@@ -328,13 +327,13 @@ __device__ __forceinline__ void gemm1_tile(const GPool& pool, const uint8_t* __r
 
 // ------------------------------------------------------------ gemm2
 // Tile: BM pair rows x 128 hidden columns; wave w owns columns [32w, 32w+32).
-template <int BM, bool ONLY4>
+template <int BM>
 __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, const float* __restrict__ topk_w,
                                            const int32_t* __restrict__ sorted_pair,
                                            const int32_t* __restrict__ block_slot,
                                            const int32_t* __restrict__ n_padded, int H, int I,
                                            const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-                                           uint16_t* __restrict__ ybuf, int int4_only, const int mt_idx,
+                                           uint16_t* __restrict__ ybuf, const int mt_idx,
                                            const int nt_idx) {
     constexpr int MT = BM / 16;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -344,7 +343,6 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
     const int slot = usable_slot(block_slot[mt_idx], pool.n_slots, pool.fmt_ok, pool.fmt);
     const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, m = lane & 15, q = lane >> 4;
     const int n0 = nt_idx * 128;
-    if (int4_only && slot >= 0 && pool.fmt[slot] != 1) return;   // FP8: elsewhere
     if (slot < 0) {                                   // unusable slot (e.g. not resident): its pairs add zero
         if (block_slot[mt_idx] == MOE_SLOT_DEFERRED) return;   // (a deferred block's rows are left as they are)
         for (int i = threadIdx.x; i < BM * 16; i += GT) {
@@ -355,8 +353,8 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
         return;
     }
     const uint8_t* sb = pool.base + (size_t)slot * pool.stride;
-    // int4 needs inter % 128 == 0; the int4-only instance has no FP8 path
-    const int fmt = ONLY4 ? 1 : (int)pool.fmt[slot];
+    // (int4 needs inter % 128 == 0)
+    const int fmt = (int)pool.fmt[slot];
     const int hgroups = (I + MOE_ACT_G - 1) / MOE_ACT_G;
     const int wgroups = I / MOE_INT4_G;
     f32x4 acc[MT][2];
@@ -380,8 +378,7 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
         for (int u = 0; u < NA; ++u) {
             const int i = threadIdx.x + u * GT, r = i >> 3, ch = i & 7;
             const uint8_t* src = hq + (size_t)(mt_idx * BM + r) * I + k0 + ch * 16;
-            if constexpr (ONLY4) va[u] = *(const i32x4*)src;   // inter % 128 == 0: every chunk is valid
-            else va[u] = ch * 16 < kv ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+            va[u] = ch * 16 < kv ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -475,28 +472,15 @@ __device__ __forceinline__ void gemm2_tile(const GPool& pool, int NP, int k, con
 }
 
 // ------------------------------------------------------------ kernels
-// Grid (column tiles, blocks). With `list`, the workgroups of each column
-// take the listed blocks (count *n_list) in turn instead of block y.
+// Grid (column tiles, blocks).
 template <int BM>
 __global__ void __launch_bounds__(GT) gemm1_fp8_kernel(GPool pool, const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int NP, int k,
                                                       const int32_t* __restrict__ sorted_pair,
                                                       const int32_t* __restrict__ block_slot,
                                                       const int32_t* __restrict__ n_padded, int H, int I,
-                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-                                                      int int4_only, const int* __restrict__ list,
-                                                      const int* __restrict__ n_list) {
-    if (list == nullptr) {
-        gemm1_tile<BM, false>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, blockIdx.y,
-                       blockIdx.x);
-        return;
-    }
-    const int n = *n_list;
-    for (int i = blockIdx.y; i < n; i += gridDim.y) {
-        gemm1_tile<BM, true>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, int4_only, list[i],
-                       blockIdx.x);
-        __syncthreads();
-    }
+                                                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+    gemm1_tile<BM>(pool, xq, xs, NP, k, sorted_pair, block_slot, n_padded, H, I, hq, hs, blockIdx.y, blockIdx.x);
 }
 
 template <int BM>
@@ -505,19 +489,9 @@ __global__ void __launch_bounds__(GT, 2) gemm2_fp8_kernel(GPool pool, int NP, in
                                                       const int32_t* __restrict__ block_slot,
                                                       const int32_t* __restrict__ n_padded, int H, int I,
                                                       const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-                                                      uint16_t* __restrict__ ybuf, int int4_only,
-                                                      const int* __restrict__ list, const int* __restrict__ n_list) {
-    if (list == nullptr) {
-        gemm2_tile<BM, false>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
-                              blockIdx.y, blockIdx.x);
-        return;
-    }
-    const int n = *n_list;
-    for (int i = blockIdx.y; i < n; i += gridDim.y) {
-        gemm2_tile<BM, true>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, int4_only,
-                             list[i], blockIdx.x);
-        __syncthreads();
-    }
+                                                      uint16_t* __restrict__ ybuf) {
+    gemm2_tile<BM>(pool, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hq, hs, ybuf, blockIdx.y,
+                   blockIdx.x);
 }
 
 // ------------------------------------------------------------ host side
@@ -572,13 +546,14 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
     size_t sm1 = gemm1_smem<BM>(H);
     dim3 g2(H / 128, cap / BM);
     hipError_t e;
-    if (BM == 128 && mfma_path_ok(H, I)) {
-        // FP8 blocks on the pipelined kernels; int4 and non-resident blocks on the simple ones
-        // the prep kernel also lists the other blocks (int4 or not resident)
+    if (BM == 128 && mfma_path_ok(H, I)) {          // (int4_ring_ok(H, I) then holds too)
+        // FP8 blocks on the pipelined matrix-core kernels; the prep kernel
+        // (first of them) lists the other blocks (int4 or not usable), which
+        // run on the int4 ring kernels (those write zero rows for unusable ones)
         const int* olist = nullptr;
         const int* n_olist = nullptr;
         mfma_other_list(w.mm, H, cap, &olist, &n_olist);
-        const int oy = cap / BM < 512 ? cap / BM : 512;     // listed blocks side by side, idle rows exit at once
+        const int oy = cap / BM < 512 ? cap / BM : 512;     // bound on the listed blocks
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 0, stream);
         if (e != hipSuccess) return e;
@@ -586,30 +561,19 @@ static hipError_t launch_grouped_bm(const PoolArgs& pa, const GPool& gp, const G
         const float* wsort = nullptr;
         const uint8_t* scl = nullptr;
         mfma_prep_arrays(w.mm, cap, &tokrow, &wsort, &scl);
-        if (int4_ring_ok(H, I)) {
-            e = launch_gemm1_int4_ring(pa, w.xq, tokrow, scl, block_slot, I, w.hq, w.hs, olist, n_olist, oy, stream);
-            if (e != hipSuccess) return e;
-        } else {
-            MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, dim3(g1.x, oy), dim3(GT), sm1, stream, gp, w.xq,
-                       w.xs, NP, k, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 1, olist, n_olist);
-        }
+        e = launch_gemm1_int4_ring(pa, w.xq, tokrow, scl, block_slot, I, w.hq, w.hs, olist, n_olist, oy, stream);
+        if (e != hipSuccess) return e;
         e = launch_mfma_ffn(pa, w.xq, w.xs, NP, k, topk_w, sorted_pair, block_slot, n_padded, cap, w.hq, w.hs,
                             w.ybuf, w.mm, 1, stream);
         if (e != hipSuccess) return e;
-        if (int4_ring_ok(H, I)) {
-            e = launch_gemm2_int4_ring(pa, NP, wsort, sorted_pair, block_slot, I, w.hq, w.hs, w.ybuf, olist, n_olist,
-                                       oy, stream);
-            if (e != hipSuccess) return e;
-        } else {
-            MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, dim3(g2.x, oy), dim3(GT), gemm2_smem<BM>(), stream,
-                       gp, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 1, olist,
-                       n_olist);
-        }
+        e = launch_gemm2_int4_ring(pa, NP, wsort, sorted_pair, block_slot, I, w.hq, w.hs, w.ybuf, olist, n_olist, oy,
+                                   stream);
+        if (e != hipSuccess) return e;
     } else {
         MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_fp8_kernel<BM>, g1, dim3(GT), sm1, stream, gp, w.xq, w.xs, NP, k,
-                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, 0, nullptr, nullptr);
+                   sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs);
         MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_fp8_kernel<BM>, g2, dim3(GT), gemm2_smem<BM>(), stream, gp, NP, k,
-                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf, 0, nullptr, nullptr);
+                   topk_w, sorted_pair, block_slot, n_padded, H, I, w.hq, w.hs, w.ybuf);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

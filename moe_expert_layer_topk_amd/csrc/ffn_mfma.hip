@@ -47,8 +47,8 @@
 //   scalar loads).
 // A prep kernel lists the FP8 blocks and lays out the per-position token
 // ids, route weights and activation scales the two kernels read. Blocks whose
-// slot is int4-g128 or not resident are handled by the simpler kernels of
-// ffn_grouped.hip in their int4-only mode.
+// slot is int4-g128 or not usable are handled by the int4 ring kernels of
+// ffn_int4.hip.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
