@@ -65,6 +65,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources a kernel's byte counters depend on: counters taken for one
+# version of these files say nothing about another
+KERNEL_SOURCES = {
+    "gemm1_stream": ("ffn_stream.hip", "moe_common.h"),
+    "gemm2_stream": ("ffn_stream.hip", "moe_common.h"),
+    "combine": ("ffn_stream.hip",),
+    "gemm1_fp8": ("ffn_mfma.hip", "moe_common.h"),
+    "gemm2_fp8": ("ffn_mfma.hip", "moe_common.h"),
+    "gemm1_tile": ("ffn_int4.hip", "ffn_grouped.hip", "moe_common.h"),
+    "gemm2_tile": ("ffn_int4.hip", "ffn_grouped.hip", "moe_common.h"),
+}
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -255,8 +268,7 @@ def measure(args, name, T, L, cpu_seconds, mfma_bound):
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         rec = json.load(open(tpath)).get(f"{cfg.name}-T{T}-{dom}")
-        srcs = ("ffn_stream.hip",) if act == moe.ACT_BF16 else ("ffn_mfma.hip", "ffn_grouped.hip")
-        if rec and rec.get("source_hash") == source_hash(*srcs):
+        if rec and rec.get("source_hash") == source_hash(*KERNEL_SOURCES.get(dom, ("ffn_stream.hip",))):
             traffic = rec.get("bytes_per_launch")
     roof["traffic"] = traffic
     roof["layer_frac"] = round(mfma_frac_layer if mfma_bound else hbm_frac_layer, 4)

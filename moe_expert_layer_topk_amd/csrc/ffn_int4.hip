@@ -80,9 +80,13 @@ struct Q4Pool {
     int fmt_ok;
 };
 
-// Grid (I / 128 column tiles, y), about two workgroups per CU: the
-// workgroups of a column tile take the halves of the listed blocks (count
-// *n_list, known only on the device) in turn; FP8 blocks in the list are skipped
+// One-dimensional grid, a multiple of 8 workgroups (about two per CU).
+// Workgroups are dealt to the 8 XCDs in turn (workgroup g on XCD g % 8), and
+// every tile of a listed block (I / 128 column tiles x 2 row halves) goes to
+// the same XCD, so the halves' shared weight rows and the column tiles'
+// shared activation rows meet in that XCD's L2: XCD x takes listed blocks
+// x, x + 8, ... (count *n_list, known only on the device), its workgroups
+// their tiles in turn. FP8 blocks in the list are skipped
 // (the list also holds blocks whose slot is not usable: their pairs get zero
 // rows from the down kernel).
 __global__ void __launch_bounds__(Q_THREADS, 2)
@@ -96,15 +100,20 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
     const int m = lane & 15, q = lane >> 4;
     const int S = H / 128;                        // K steps = groups of the activation and of W13
     const int hgroups = I / 128;
-    const int c0 = blockIdx.x * 128;
+    const int NT = I / 128;                       // column tiles of a block
+    const int xcd = blockIdx.x & 7, P = gridDim.x >> 3;
     uint8_t* s_xs = smem + Q_XS;
     const int fm = qsw(m);
     const int o0 = ((2 * q) ^ fm) << 4, o1 = ((2 * q + 1) ^ fm) << 4;
 
     const int n = *n_list;
-    for (int li = blockIdx.y; li < 2 * n; li += gridDim.y) {
-        const int b = list[li >> 1];
-        const int r0 = b * Q_BM + (li & 1) * Q_TM;   // first sorted position of the tile
+    for (int j = blockIdx.x >> 3;; j += P) {
+        const int bi = xcd + 8 * (j / (2 * NT));      // listed block, column tile, row half of tile j
+        if (bi >= n) break;
+        const int ct = (j % (2 * NT)) >> 1, half = j & 1;
+        const int c0 = ct * 128;
+        const int b = list[bi];
+        const int r0 = b * Q_BM + half * Q_TM;        // first sorted position of the tile
         const int slot = usable_slot(block_slot[b], pool.n_slots, pool.fmt_ok, pool.fmt);
         if (slot < 0 || pool.fmt[slot] != MOE_FMT_INT4_G128) continue;   // (uniform over the workgroup)
         const uint8_t* w13 = pool.base + (size_t)slot * pool.stride;   // int4 codes [2I][H/2]
@@ -116,7 +125,7 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
 #pragma unroll
         for (int v = 0; v < Q_TM * 16 / 4 / Q_THREADS; ++v) {
             const int i = threadIdx.x + Q_THREADS * v, g = i >> 4, r4 = (i & 15) * 4;   // 4 rows of step g
-            xsw[v] = g < S ? *(const uint32_t*)(scl + ((size_t)b * S + g) * Q_BM + (li & 1) * Q_TM + r4) : 0u;
+            xsw[v] = g < S ? *(const uint32_t*)(scl + ((size_t)b * S + g) * Q_BM + half * Q_TM + r4) : 0u;
         }
         // the loads of step g into stage u: wave w fills activation rows
         // 16w .. 16w + 15 and its own weight rows (local row lr < 32: gate
@@ -299,7 +308,7 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
                     sH[row * Q_HROW + wv * 32 + c * 16 + m] = (uint8_t)(f32x2_to_e4m3(ldexpf(hv[a][c][i], -e), 0.f) & 0xFF);
-                if (wv == 0 && m == 0) hs[(size_t)(r0 + row) * hgroups + blockIdx.x] = (uint8_t)(e + 127);
+                if (wv == 0 && m == 0) hs[(size_t)(r0 + row) * hgroups + ct] = (uint8_t)(e + 127);
             }
         __syncthreads();
         for (int i = threadIdx.x; i < Q_TM * 8; i += Q_THREADS) {
@@ -353,7 +362,8 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
     const int m = lane & 15, q = lane >> 4;
     const int S = I / 128;                        // K steps = groups of h and of W2
-    const int n0 = blockIdx.x * 128;
+    const int NT = H / 128;                       // column tiles of a block
+    const int xcd = blockIdx.x & 7, P = gridDim.x >> 3;
     uint8_t* s_hs = smem + D_HS;
     int* s_pr = (int*)(smem + D_PR);
     float* s_w = (float*)(smem + D_W);
@@ -361,8 +371,13 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
     const int o0 = ((2 * q) ^ fm) << 4, o1 = ((2 * q + 1) ^ fm) << 4;
 
     const int n = *n_list;
-    for (int li = blockIdx.y; li < n; li += gridDim.y) {
-        const int b = list[li];
+    // XCD x takes listed blocks x, x + 8, ..., its workgroups their column
+    // tiles in turn (a block's h rows meet in that XCD's L2)
+    for (int j = blockIdx.x >> 3;; j += P) {
+        const int bi = xcd + 8 * (j / NT);
+        if (bi >= n) break;
+        const int n0 = (j % NT) * 128;
+        const int b = list[bi];
         const int bs = block_slot[b];
         const int slot = usable_slot(bs, pool.n_slots, pool.fmt_ok, pool.fmt);
         if (slot < 0) {                           // not usable: the block's pairs add zero
@@ -550,8 +565,9 @@ hipError_t launch_gemm1_int4_ring(const PoolArgs& pa, const uint8_t* xq, const i
     hipError_t e = hipFuncSetAttribute((const void*)gemm1_int4_ring_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        Q_SMEM);
     if (e != hipSuccess) return e;
-    const int gy = min(2 * grid_y, max(1, 2 * device_cus() / (I / 128)));
-    MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_int4_ring_kernel, dim3(I / 128, gy), dim3(Q_THREADS), Q_SMEM, stream, qp,
+    // about two workgroups per CU, a multiple of 8, no more than the tiles can use
+    const int g = max(8, min(2 * device_cus(), 2 * (I / 128) * grid_y) / 8 * 8);
+    MOE_LAUNCH(K_GEMM1_TILE, stream, gemm1_int4_ring_kernel, dim3(g), dim3(Q_THREADS), Q_SMEM, stream, qp,
                xq, tokrow, scl, block_slot, pa.hidden, I, hq, hs, list, n_list);
     return hipGetLastError();
 }
@@ -571,8 +587,8 @@ hipError_t launch_gemm2_int4_ring(const PoolArgs& pa, int NP, const float* wsort
     hipError_t e = hipFuncSetAttribute((const void*)gemm2_int4_ring_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        D_SMEM);
     if (e != hipSuccess) return e;
-    const int gy = min(grid_y, max(1, 2 * device_cus() / (pa.hidden / 128)));
-    MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_int4_ring_kernel, dim3(pa.hidden / 128, gy), dim3(Q_THREADS), D_SMEM,
+    const int g = max(8, min(2 * device_cus(), (pa.hidden / 128) * grid_y) / 8 * 8);
+    MOE_LAUNCH(K_GEMM2_TILE, stream, gemm2_int4_ring_kernel, dim3(g), dim3(Q_THREADS), D_SMEM,
                stream, qp, NP, wsort, sorted_pair, block_slot, pa.hidden, I, hq, hs, ybuf, list, n_list);
     return hipGetLastError();
 }

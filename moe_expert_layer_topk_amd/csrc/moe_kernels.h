@@ -122,7 +122,8 @@ void set_debug_poison(int on);
 bool debug_poison_on();
 hipError_t launch_poison(void* p, size_t bytes, hipStream_t stream);
 
-// int4 blocks listed beside the FP8 matrix-core kernels, gate/up GEMM on an
+// int4 blocks listed beside the FP8 matrix-core kernels (grid_y: a bound on
+// the listed blocks), gate/up GEMM on an
 // LDS ring (H and I multiples of 128 up to 2048)
 bool int4_ring_ok(int H, int I);
 hipError_t launch_gemm1_int4_ring(const PoolArgs& pa, const uint8_t* xq, const int32_t* tokrow, const uint8_t* scl,
