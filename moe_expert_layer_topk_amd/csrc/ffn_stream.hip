@@ -671,8 +671,16 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
 // FUSE 0: the block tables come from a separate align launch. FUSE 1: the
 // pairs are sorted here from the route results (layer_prologue). FUSE 2: the
 // tokens are routed here too (route_select<RVPL>).
+// FUSE 0 and 1 run one workgroup per CU with the weights of the unit two
+// ahead in flight (three register sets): one set-up per CU instead of two,
+// and one unit stream per CU, which ends evenly (two workgroups per CU each
+// sorted the pairs, the second one's set-up took twice as long, and it ended
+// several microseconds after the first). FUSE 2, whose set-up routes the
+// tokens, keeps two workgroups per CU and one unit of prefetch.
+constexpr int gemm1_pipe_wgs_per_cu(int fuse) { return fuse == 2 ? 2 : 1; }
+
 template <int FUSE, int RVPL, int RT>
-__global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
+__global__ void __launch_bounds__(G_THREADS, gemm1_pipe_wgs_per_cu(FUSE)) gemm1_pipe_kernel(
     SlotView pool, int n_slots, const uint16_t* __restrict__ x, int T, int k,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
     const int32_t* __restrict__ n_padded, int H, int I, uint16_t* __restrict__ hbuf, LayerIO L) {
@@ -685,7 +693,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     const int ntile = I / P1_ROWS;
     const int groups = H / 128;
     const int NP = T * k;
-    P1W WA, WB;
+    constexpr int PF = gemm1_pipe_wgs_per_cu(FUSE) == 1 ? 2 : 1;   // units of prefetch
+    P1W WA, WB, WC;
     P1X X;
     int xblock = -1;
     int u_begin, u_end, b_first, nblk;
@@ -735,6 +744,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             p1_landed(WA);
             p1_issue_w(WA, pool, s0, s_fmt[s0], (u_begin % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
+        if constexpr (PF == 2) {
+            const int u1 = min(u_begin + 1, u_end - 1), s1 = s_slot[u1 / ntile - b_first];
+            p1_issue_w(WB, pool, pf_slot(s1), pf_fmt(s1), (u1 % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        }
     } else {
         const P1Range R = layer_prologue<RVPL, RT>(L, pool.fmt, n_slots, pool.fmt_ok, pool.spec_fmt, T, k, ntile, s_fmt,
                                                    s_slot, s_pr);
@@ -746,6 +759,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
         barrier_lds();
         p1_issue_w(WA, pool, pf_slot(s_slot[0]), pf_fmt(s_slot[0]), (u_begin % ntile) * P1_ROWS, m, q, wv, H, I,
                    groups);
+        if constexpr (PF == 2) {
+            const int u1 = min(u_begin + 1, u_end - 1), s1 = s_slot[u1 / ntile - b_first];
+            p1_issue_w(WB, pool, pf_slot(s1), pf_fmt(s1), (u1 % ntile) * P1_ROWS, m, q, wv, H, I, groups);
+        }
     }
     auto step = [&](int u, P1W& Wc, P1W& Wn) {
         const int bb = u / ntile - b_first;
@@ -759,9 +776,9 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
             xblock = bb;
         }
         {
-            // the next unit's weights (slot 0 for an unusable slot, whose unit
-            // ignores them; past the range: this unit again)
-            const int un = min(u + 1, u_end - 1);
+            // the weights of unit u + PF (slot 0 for an unusable slot, whose
+            // unit ignores them; past the range: the last unit again)
+            const int un = min(u + PF, u_end - 1);
             const int sn = s_slot[un / ntile - b_first];
             p1_issue_w(Wn, pool, pf_slot(sn), pf_fmt(sn), (un % ntile) * P1_ROWS, m, q, wv, H, I, groups);
         }
@@ -799,11 +816,21 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm1_pipe_kernel(
     // set's loads pending there, and the compiler would then wait for every
     // load in flight at the head of each iteration (the prefetch included)
     int u = u_begin;
-    for (; u + 1 < u_end; u += 2) {
-        step(u, WA, WB);
-        step(u + 1, WB, WA);
+    if constexpr (PF == 2) {                          // three register sets in turn
+        for (; u + 2 < u_end; u += 3) {
+            step(u, WA, WC);
+            step(u + 1, WB, WA);
+            step(u + 2, WC, WB);
+        }
+        if (u < u_end) step(u, WA, WC);
+        if (u + 1 < u_end) step(u + 1, WB, WA);
+    } else {
+        for (; u + 1 < u_end; u += 2) {
+            step(u, WA, WB);
+            step(u + 1, WB, WA);
+        }
+        if (u < u_end) step(u, WA, WB);
     }
-    if (u < u_end) step(u, WA, WB);
 }
 
 // ------------------------------------------------------------ gemm2
@@ -1319,7 +1346,7 @@ static void launch_stream_bm(const SlotView& sv, int n_slots, const uint16_t* x,
     const int NP = T * k;
     const int nb = cap / BM;                        // blocks that can exist; the kernels skip the rest
     const int units = nb * (I / ROWS);
-    const int pipe_grid = 2 * device_cus();
+    const int pipe_grid = gemm1_pipe_wgs_per_cu(0) * device_cus();
     // the pipelined kernel: 16-pair blocks, hidden <= 2048, and each workgroup's
     // unit range must span at most P1_MAXB blocks (always true unless the grid is tiny)
     const int pipe_units = nb * (I / P1_ROWS);
@@ -1373,7 +1400,7 @@ size_t layer_stream_workspace_bytes(int T, int k, int H, int I, int cap) {
 bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
     if (block_m != 16 || T > LAYER_MAX_T || T * k > LAYER_MAX_NP || E > MOE_MAX_E) return false;
     if (H > 128 * G_WAVES * P1_G) return false;
-    const int pipe_grid = 2 * device_cus();
+    const int pipe_grid = device_cus();              // (the smaller of the gate/up grids: the longer ranges)
     const int per = max_units((cap / 16) * (I / P1_ROWS), pipe_grid);
     return per / (I / P1_ROWS) + 2 <= P1_MAXB;
 }
@@ -1381,7 +1408,8 @@ bool layer_stream_ok(int T, int k, int E, int H, int I, int block_m, int cap) {
 template <int RVPL, int RT>
 static void launch_gemm1_layer(const SlotView& sv, int n_slots, const uint16_t* x, int T, int k, int H, int I,
                                uint16_t* hbuf, const LayerIO& L, hipStream_t stream) {
-    MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<RVPL == 0 ? 1 : 2, RVPL, RT>), dim3(2 * device_cus()),
+    MOE_LAUNCH(K_GEMM1_STREAM, stream, (gemm1_pipe_kernel<RVPL == 0 ? 1 : 2, RVPL, RT>),
+               dim3(gemm1_pipe_wgs_per_cu(RVPL == 0 ? 1 : 2) * device_cus()),
                dim3(G_THREADS), 0, stream, sv, n_slots, x, T, k, (const int32_t*)nullptr, (const int32_t*)nullptr,
                (const int32_t*)nullptr, H, I, hbuf, L);
 }
