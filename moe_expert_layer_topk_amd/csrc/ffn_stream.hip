@@ -1041,8 +1041,14 @@ __device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, int f
 // GD: the unit range and the first block's slot and format come from the
 // descriptor the gate/up kernel wrote (whole-layer call), so the first
 // weights are loaded in the same round trip as the tables.
+// Twelve K chunks (inter 640 or 768): one workgroup per CU with the weights of
+// the unit two ahead in flight; at two workgroups per CU the h rows and two
+// weight register sets spilled. Eight chunks: two workgroups per CU, one unit
+// of prefetch (one per CU measured slower at 8 tokens).
+constexpr int gemm2_pipe_wgs_per_cu(int chunks) { return chunks == 12 ? 1 : 2; }
+
 template <int P2_C, bool GD>
-__global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
+__global__ void __launch_bounds__(G_THREADS, gemm2_pipe_wgs_per_cu(P2_C)) gemm2_pipe_kernel(
     SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
     const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf,
@@ -1073,7 +1079,8 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     auto ok = [&](int slot) { return usable_slot(slot, n_slots, pool.fmt_ok, s_fmt); };
     auto pf_slot = [&](int slot) { return max(ok(slot), 0); };
     auto pf_fmt = [&](int slot) { const int s = ok(slot); return s >= 0 ? (int)s_fmt[s] : pool.spec_fmt; };
-    P2W<P2_C> WA, WB;
+    constexpr int PF = gemm2_pipe_wgs_per_cu(P2_C) == 1 ? 2 : 1;   // units of prefetch
+    P2W<P2_C> WA, WB, WC;
     P2H<P2_C> Hh;
     int hblock = -1;
     float wt = 0.f;
@@ -1102,6 +1109,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         }
         for (int i = i1; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];       // pools over 256 slots
         barrier_lds();                               // tables written; the weight loads stay in flight
+        if constexpr (PF == 2) {
+            const int u1 = min(u_begin + 1, u_end - 1), s1 = s_slot[u1 / ntile - b_first];
+            p2_issue_w(WB, pool, pf_slot(s1), pf_fmt(s1), (u1 % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        }
     } else {
         for (int i = threadIdx.x; i < n_slots; i += G_THREADS) s_fmt[i] = pool.fmt[i];
         for (int i = threadIdx.x; i < nblk * 17; i += G_THREADS) {
@@ -1113,6 +1124,10 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
         if (nblk == 0) return;
         const int s0 = s_slot[0];
         p2_issue_w(WA, pool, pf_slot(s0), pf_fmt(s0), (u_begin % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        if constexpr (PF == 2) {
+            const int u1 = min(u_begin + 1, u_end - 1), s1 = s_slot[u1 / ntile - b_first];
+            p2_issue_w(WB, pool, pf_slot(s1), pf_fmt(s1), (u1 % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
+        }
     }
     auto step = [&](int u, P2W<P2_C>& Wc, P2W<P2_C>& Wn) {
         const int bb = u / ntile - b_first;
@@ -1127,11 +1142,11 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
             hblock = bb;
         }
         {
-            // the next unit's weights, with no branch around the loads (slot 0
-            // for an unusable slot, whose unit ignores them; past the range:
-            // this unit again), so the compiler's count of loads in flight
-            // stays exact and the wait below leaves them in flight
-            const int un = min(u + 1, u_end - 1);
+            // the weights of unit u + PF, with no branch around the loads
+            // (slot 0 for an unusable slot, whose unit ignores them; past the
+            // range: the last unit again), so the compiler's count of loads
+            // in flight stays exact and the wait below leaves them in flight
+            const int un = min(u + PF, u_end - 1);
             const int sn = s_slot[un / ntile - b_first];
             p2_issue_w(Wn, pool, pf_slot(sn), pf_fmt(sn), (un % ntile) * G2_COLS + wv * 16, m, q, I, chunks);
         }
@@ -1191,11 +1206,21 @@ __global__ void __launch_bounds__(G_THREADS, 2) gemm2_pipe_kernel(
     // set's loads pending there, and the compiler would then wait for every
     // load in flight at the head of each iteration (the prefetch included)
     int u = u_begin;
-    for (; u + 1 < u_end; u += 2) {
-        step(u, WA, WB);
-        step(u + 1, WB, WA);
+    if constexpr (PF == 2) {                          // three register sets in turn
+        for (; u + 2 < u_end; u += 3) {
+            step(u, WA, WC);
+            step(u + 1, WB, WA);
+            step(u + 2, WC, WB);
+        }
+        if (u < u_end) step(u, WA, WC);
+        if (u + 1 < u_end) step(u + 1, WB, WA);
+    } else {
+        for (; u + 1 < u_end; u += 2) {
+            step(u, WA, WB);
+            step(u + 1, WB, WA);
+        }
+        if (u < u_end) step(u, WA, WB);
     }
-    if (u < u_end) step(u, WA, WB);
 }
 
 // ------------------------------------------------------------ combine
@@ -1309,6 +1334,10 @@ size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
     return up256((size_t)cap * I * sizeof(uint16_t)) + up256((size_t)T * k * H * sizeof(float));
 }
 
+// the down kernel's grid (the gate/up kernel of a whole-layer call writes one
+// descriptor per workgroup of it)
+static int gemm2_pipe_grid(int I) { return gemm2_pipe_wgs_per_cu(I > 64 * 8 ? 12 : 8) * device_cus(); }
+
 template <int BM>
 static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, const float* topk_w,
                                 const int32_t* sorted_pair, const int32_t* block_slot, const int32_t* n_padded,
@@ -1316,7 +1345,7 @@ static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, c
                                 const int4* gdesc = nullptr) {
     const int NP = T * k;
     const int nb = cap / BM;
-    const int pipe_grid = 2 * device_cus();
+    const int pipe_grid = gemm2_pipe_grid(I);
     const int units2 = nb * (H / G2_COLS);
     const int per2 = max_units(units2, pipe_grid);
     if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
@@ -1445,7 +1474,7 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
         if (e != hipSuccess) return e;
     }
     LayerIO L{logits, mask,     slot_of_expert, E,          ids,         w,          sorted_pair,
-              block_slot, counts, seg_offset, n_padded, err, gdesc, 2 * device_cus(), H};
+              block_slot, counts, seg_offset, n_padded, err, gdesc, gemm2_pipe_grid(I), H};
     if (T <= LAYER_ROUTE_MAX_T && E <= 512) {
         if (E <= 256) launch_gemm1_route<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
         else launch_gemm1_route<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
