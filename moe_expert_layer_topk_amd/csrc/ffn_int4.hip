@@ -196,8 +196,10 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
 #pragma unroll
             for (int d = 0; d < 4; ++d) s_xs[(r4 + d) * 16 + g] = (uint8_t)(xsw[v] >> (8 * d));
         }
-        i32x8 bf[2][2];                               // e4m3 codes of q - zero of the current step
-        float sc[2][2];                               // their group scales (this lane's output columns)
+        // e4m3 codes of q - zero and group scales (this lane's output
+        // columns) of a step: two sets, current and next, in turn
+        i32x8 bfA[2][2], bfB[2][2];
+        float scA[2][2], scB[2][2];
         {
             wait_vmcnt<2 * Q_OPS>();                  // this wave's stage 0
             i32x4 raw[2][2];
@@ -207,11 +209,12 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
             for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    convert(raw[gu][c], zs[gu][c], bf[gu][c]);
-                    sc[gu][c] = f16_lo(zs[gu][c]);
+                    convert(raw[gu][c], zs[gu][c], bfA[gu][c]);
+                    scA[gu][c] = f16_lo(zs[gu][c]);
                 }
         }
-        for (int g = 0; g < S; ++g) {
+        auto step = [&](int g, const i32x8 (&bf)[2][2], const float (&sc)[2][2], i32x8 (&bn)[2][2],
+                        float (&scn)[2][2]) __attribute__((always_inline)) {
             const int u = g % Q_RING, un = (g + 1) % Q_RING;
             const uint8_t* st = smem + u * Q_STAGE;
             wait_vmcnt<Q_OPS>();                      // this wave's stages g and g + 1 (step g + 2 may fly)
@@ -233,7 +236,6 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
             // the loads of step g + 3 into stage u (past the end: the last
             // step again, so every step leaves the same number of loads behind)
             const int gl = min(g + Q_RING, S - 1);
-            i32x8 bn[2][2];
             f32x4 t4[2][2][2];
 #pragma unroll
             for (int a = 0; a < 5; ++a) {
@@ -259,11 +261,15 @@ __global__ void __launch_bounds__(Q_THREADS, 2)
 #pragma unroll
             for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    bf[gu][c] = bn[gu][c];
-                    sc[gu][c] = f16_lo(zs[gu][c]);
-                }
+                for (int c = 0; c < 2; ++c) scn[gu][c] = f16_lo(zs[gu][c]);
+        };
+        // steps in pairs (the sets swap roles), then an odd last one
+        int g = 0;
+        for (; g + 1 < S; g += 2) {
+            step(g, bfA, scA, bfB, scB);
+            step(g + 1, bfB, scB, bfA, scA);
         }
+        if (g < S) step(g, bfA, scA, bfB, scB);
         wait_vmcnt<0>();
         __syncthreads();
 
