@@ -1043,12 +1043,14 @@ __device__ __forceinline__ void p2_issue_h(P2H<C>& Hh, const uint16_t* hr, int f
 // weights are loaded in the same round trip as the tables.
 // Twelve K chunks (inter 640 or 768): one workgroup per CU with the weights of
 // the unit two ahead in flight; at two workgroups per CU the h rows and two
-// weight register sets spilled. Eight chunks: two workgroups per CU, one unit
-// of prefetch (one per CU measured slower at 8 tokens).
+// weight register sets spilled. Eight chunks: the same from 256 pairs up (its
+// longer unit ranges end more evenly: 0.7 us less at 32 tokens x 8), two
+// workgroups per CU with one unit of prefetch below (one per CU measured
+// 0.4-1.4 us slower at 8 tokens). WPC = workgroups per CU.
 constexpr int gemm2_pipe_wgs_per_cu(int chunks) { return chunks == 12 ? 1 : 2; }
 
-template <int P2_C, bool GD>
-__global__ void __launch_bounds__(G_THREADS, gemm2_pipe_wgs_per_cu(P2_C)) gemm2_pipe_kernel(
+template <int P2_C, bool GD, int WPC = gemm2_pipe_wgs_per_cu(P2_C)>
+__global__ void __launch_bounds__(G_THREADS, WPC) gemm2_pipe_kernel(
     SlotView pool, int n_slots, int NP, int k, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ block_slot,
     const int32_t* __restrict__ n_padded, int H, int I, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf,
@@ -1079,7 +1081,7 @@ __global__ void __launch_bounds__(G_THREADS, gemm2_pipe_wgs_per_cu(P2_C)) gemm2_
     auto ok = [&](int slot) { return usable_slot(slot, n_slots, pool.fmt_ok, s_fmt); };
     auto pf_slot = [&](int slot) { return max(ok(slot), 0); };
     auto pf_fmt = [&](int slot) { const int s = ok(slot); return s >= 0 ? (int)s_fmt[s] : pool.spec_fmt; };
-    constexpr int PF = gemm2_pipe_wgs_per_cu(P2_C) == 1 ? 2 : 1;   // units of prefetch
+    constexpr int PF = WPC == 1 ? 2 : 1;            // units of prefetch
     P2W<P2_C> WA, WB, WC;
     P2H<P2_C> Hh;
     int hblock = -1;
@@ -1336,7 +1338,8 @@ size_t stream_workspace_bytes(int T, int k, int H, int I, int cap) {
 
 // the down kernel's grid (the gate/up kernel of a whole-layer call writes one
 // descriptor per workgroup of it)
-static int gemm2_pipe_grid(int I) { return gemm2_pipe_wgs_per_cu(I > 64 * 8 ? 12 : 8) * device_cus(); }
+static int gemm2_pipe_wpc(int I, int NP) { return I > 64 * 8 || NP >= 256 ? 1 : 2; }
+static int gemm2_pipe_grid(int I, int NP) { return gemm2_pipe_wpc(I, NP) * device_cus(); }
 
 template <int BM>
 static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, const float* topk_w,
@@ -1345,13 +1348,19 @@ static void launch_gemm2_stream(const SlotView& sv, int n_slots, int T, int k, c
                                 const int4* gdesc = nullptr) {
     const int NP = T * k;
     const int nb = cap / BM;
-    const int pipe_grid = gemm2_pipe_grid(I);
+    const int pipe_grid = gemm2_pipe_grid(I, NP);
     const int units2 = nb * (H / G2_COLS);
     const int per2 = max_units(units2, pipe_grid);
     if (BM == 16 && I <= 64 * 8 && per2 / (H / G2_COLS) + 2 <= P2_MAXB) {
-        if (gdesc)
+        if (gdesc && pipe_grid == device_cus())
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, true, 1>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
+                       sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
+        else if (gdesc)
             MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, true>), dim3(pipe_grid), dim3(G_THREADS), 0, stream,
                        sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
+        else if (pipe_grid == device_cus())
+            MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, false, 1>), dim3(pipe_grid), dim3(G_THREADS), 0,
+                       stream, sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
         else
             MOE_LAUNCH(K_GEMM2_STREAM, stream, (gemm2_pipe_kernel<8, false>), dim3(pipe_grid), dim3(G_THREADS), 0,
                        stream, sv, n_slots, NP, k, topk_w, sorted_pair, block_slot, n_padded, H, I, hbuf, ybuf, gdesc);
@@ -1474,7 +1483,7 @@ hipError_t launch_layer_stream(const PoolArgs& pa, const float* logits, const ui
         if (e != hipSuccess) return e;
     }
     LayerIO L{logits, mask,     slot_of_expert, E,          ids,         w,          sorted_pair,
-              block_slot, counts, seg_offset, n_padded, err, gdesc, gemm2_pipe_grid(I), H};
+              block_slot, counts, seg_offset, n_padded, err, gdesc, gemm2_pipe_grid(I, T * k), H};
     if (T <= LAYER_ROUTE_MAX_T && E <= 512) {
         if (E <= 256) launch_gemm1_route<4>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
         else launch_gemm1_route<8>(sv, pa.n_slots, x, T, k, H, I, hbuf, L, stream);
