@@ -470,7 +470,12 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
     __shared__ int s_wsum[G_WAVES];
     const int tid = threadIdx.x, lane = lane_id(), wv = tid / MOE_WAVE;
     const int NP = T * k, E = L.E;
-    const bool writer = blockIdx.x == 0;
+    // the tables this call hands on, each written by one workgroup (different
+    // XCDs): counts and offsets, block slots, padding sentinels, down-kernel
+    // descriptors, sorted pairs, route results
+    const int G = gridDim.x;
+    const bool w_tab = blockIdx.x == 0, w_blk = blockIdx.x == 1 % G, w_pad = blockIdx.x == 2 % G;
+    const bool w_desc = blockIdx.x == 3 % G, w_pair = blockIdx.x == 4 % G, w_ids = blockIdx.x == 5 % G;
     // ---- every global load first (one round trip): slot table, format
     // tags, and the route ids or the logits of this wavefront's RT tokens.
     // Each load instruction holds its wave for a while as it issues, so only
@@ -533,15 +538,17 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
             if (t >= T) break;                       // uniform over the wave
             if (lane < k) {
                 s_ids[t * k + lane] = id[j];
-                if (writer) {
+                if (w_ids) {
                     L.ids[t * k + lane] = id[j];
                     L.w[t * k + lane] = wt[j];
                 }
             }
-            if (writer && lane == 0 && found[j] < k) atomicAdd(&L.err[0], 1);
+            if (w_ids && lane == 0 && found[j] < k) atomicAdd(&L.err[0], 1);
         }
     }
-    __syncthreads();
+    // (the prologue's barriers wait for LDS only: nothing here reads back the
+    // tables handed on, so their stores stay in flight)
+    barrier_lds();
     // the format tags are in LDS: a slot outside the pool or with a format
     // that does not fit the stride counts as not resident
 #pragma unroll
@@ -566,7 +573,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
             ++bad;
         }
     }
-    __syncthreads();
+    barrier_lds();
     // padded counts of this thread's experts, then their exclusive scan
     int c[LAYER_EPT], off[LAYER_EPT], sum = 0;
 #pragma unroll
@@ -584,7 +591,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         if (lane >= o) incl += y;
     }
     if (lane == MOE_WAVE - 1) s_wsum[wv] = incl;
-    __syncthreads();
+    barrier_lds();
     int base = incl - sum, total = 0;
 #pragma unroll
     for (int w2 = 0; w2 < G_WAVES; ++w2) {
@@ -598,17 +605,21 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         off[i] += base;
         if (e < E) s_off[e] = off[i];
     }
-    if (writer) {
+    if (w_tab || w_blk) {
 #pragma unroll
         for (int i = 0; i < LAYER_EPT; ++i) {
             const int e = tid * LAYER_EPT + i;
             if (e >= E) continue;
             const int pad = (c[i] + 15) & ~15;
-            L.counts[e] = c[i];
-            L.seg_offset[e] = off[i];
-            for (int b = off[i] / 16; b < (off[i] + pad) / 16; ++b) L.block_slot[b] = slot_e[i];
-            for (int q = off[i] + c[i]; q < off[i] + pad; ++q) L.sorted_pair[q] = NP;
+            if (w_tab) {
+                L.counts[e] = c[i];
+                L.seg_offset[e] = off[i];
+            }
+            if (w_blk)
+                for (int b = off[i] / 16; b < (off[i] + pad) / 16; ++b) L.block_slot[b] = slot_e[i];
         }
+    }
+    if (w_tab) {
         if (tid == 0) {
             L.seg_offset[E] = total;
             *L.n_padded = total;
@@ -630,8 +641,19 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         const int b1 = min((off[i] + ((c[i] + 15) & ~15)) / 16, R.b_first + R.nblk);
         for (int b = b0; b < b1; ++b) s_slot[b - R.b_first] = slot_e[i];
     }
-    __syncthreads();                                   // sentinels before the pairs
-    if (writer && L.gdesc) {
+    barrier_lds();                                   // sentinels before the pairs
+    if (w_pad) {
+        // padding sentinels: the tail of each expert's last block, 16 lanes
+        // per expert (one line per store instead of a lane per expert)
+        const int j = tid & 15;
+#pragma unroll 4
+        for (int e = tid >> 4; e < E; e += G_THREADS / 16) {
+            const int ce = s_cnt[e], oe = s_off[e];
+            const int q = oe + ((ce + 15) & ~15) - 16 + j;
+            if (q >= oe + ce) L.sorted_pair[q] = NP;
+        }
+    }
+    if (w_desc && L.gdesc) {
         // the down kernel's unit ranges (its units: block x 64 hidden rows)
         // with the slot and format of each range's first block, so that it
         // loads its first weights without waiting for these tables
@@ -661,7 +683,7 @@ __device__ __forceinline__ P1Range layer_prologue(const LayerIO& L, const uint8_
         if (p >= NP || e < 0 || e >= E) continue;
         const int t = p / k;
         const int pos = s_off[e] + (int)__popcll(s_tok[e] & ((1ull << t) - 1ull));
-        if (writer) L.sorted_pair[pos] = p;
+        if (w_pair) L.sorted_pair[pos] = p;
         const int bb = pos / 16 - R.b_first;
         if (bb >= 0 && bb < R.nblk) s_pr[bb][pos % 16] = p;
     }
