@@ -85,11 +85,10 @@ __device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_sl, in
         *n_padded = total;
     }
     __syncthreads();
-    // block -> slot and the sentinel tails, spread over the workgroup by
-    // block (a hot expert's segment spans many blocks): a block's expert is
-    // the last one whose segment starts at or before it (empty segments
-    // share their offset with the next expert, so the last one is never
-    // empty); only a segment's last block holds padding
+    // block -> slot, spread over the workgroup by block (a hot expert's
+    // segment spans many blocks): a block's expert is the last one whose
+    // segment starts at or before it (empty segments share their offset with
+    // the next expert, so the last one is never empty)
     for (int b = threadIdx.x; b < total / block_m; b += blockDim.x) {
         const int pos = b * block_m;
         int lo = 0, hi = E - 1;
@@ -99,7 +98,17 @@ __device__ void segments_from_counts(const int* s_cnt, int* s_off, int* s_sl, in
             else hi = mid - 1;
         }
         block_slot[b] = s_sl[lo];
-        for (int q = max(pos, s_off[lo] + s_cnt[lo]); q < pos + block_m; ++q) sorted_pair[q] = sentinel;
+    }
+    // the sentinel tails (only a segment's last block holds padding): one
+    // wave per expert, the tail's positions across the lanes, so each store
+    // covers whole lines instead of one lane's run of single positions
+    {
+        const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE, nw = blockDim.x / MOE_WAVE;
+        for (int x = wv; x < E; x += nw) {
+            const int c = s_cnt[x], o = s_off[x];
+            const int pad = (c + block_m - 1) / block_m * block_m;
+            for (int q = o + c + lane; q < o + pad; q += MOE_WAVE) sorted_pair[q] = sentinel;
+        }
     }
     __syncthreads();
 }
