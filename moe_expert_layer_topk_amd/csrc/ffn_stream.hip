@@ -1253,14 +1253,18 @@ __global__ void __launch_bounds__(G_THREADS, WPC) gemm2_pipe_kernel(
 // are skipped: their rows were never written.
 template <typename YT, int KMAX>
 __global__ void __launch_bounds__(256) combine_rows_kernel(const YT* __restrict__ ybuf, const float* __restrict__ topk_w,
-                                                          int T, int k, int H, uint16_t* __restrict__ out) {
-    // workgroups walk tokens; a token's weights are wave-uniform (scalar
-    // loads), each thread sums 8 columns of the token's k rows
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+                                                          int T, int k, int H, uint16_t* __restrict__ out,
+                                                          int pieces) {
+    // workgroups walk (token, column piece) items, H / pieces columns each; a
+    // token's weights are wave-uniform (scalar loads), each thread sums 8
+    // columns of the token's k rows
+    const int cw = H / pieces;
+    for (int it = blockIdx.x; it < T * pieces; it += gridDim.x) {
+        const int t = it / pieces, c0 = (it % pieces) * cw;
         float wj[KMAX];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) wj[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
-        for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+        for (int c = c0 + threadIdx.x * 8; c < c0 + cw; c += blockDim.x * 8) {
             float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             // every load first (rows of unfilled route entries are read but not used)
             i32x4 v[KMAX][sizeof(YT) == 4 ? 2 : 1];
@@ -1305,16 +1309,20 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(const YT* __restrict_
 
 hipError_t launch_combine_f32(const float* ybuf, const float* topk_w, int T, int k, int H, uint16_t* out,
                               hipStream_t stream) {
-    const int blocks = T < 4096 ? T : 4096;
+    // decode sizes: one wave per (token, 512 columns), so a few tokens still
+    // spread over many CUs; otherwise a 256-thread workgroup per token
+    const bool narrow = H % 512 == 0 && T * (H / 512) <= 4096;
+    const int pieces = narrow ? H / 512 : 1, threads = narrow ? MOE_WAVE : 256;
+    const int items = T * pieces, blocks = items < 4096 ? items : 4096;
     if (k <= 8)
-        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 8>), dim3(blocks), dim3(256), 0, stream, ybuf, topk_w,
-                   T, k, H, out);
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 8>), dim3(blocks), dim3(threads), 0, stream, ybuf,
+                   topk_w, T, k, H, out, pieces);
     else if (k <= 16)
-        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 16>), dim3(blocks), dim3(256), 0, stream, ybuf,
-                   topk_w, T, k, H, out);
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, 16>), dim3(blocks), dim3(threads), 0, stream, ybuf,
+                   topk_w, T, k, H, out, pieces);
     else
-        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, MOE_MAX_K>), dim3(blocks), dim3(256), 0, stream, ybuf,
-                   topk_w, T, k, H, out);
+        MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<float, MOE_MAX_K>), dim3(blocks), dim3(threads), 0, stream,
+                   ybuf, topk_w, T, k, H, out, pieces);
     return hipGetLastError();
 }
 
@@ -1323,13 +1331,13 @@ hipError_t launch_combine_bf16(const uint16_t* ybuf, const float* topk_w, int T,
     const int blocks = T < 4096 ? T : 4096;
     if (k <= 8)
         MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, 8>), dim3(blocks), dim3(256), 0, stream, ybuf,
-                   topk_w, T, k, H, out);
+                   topk_w, T, k, H, out, 1);
     else if (k <= 16)
         MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, 16>), dim3(blocks), dim3(256), 0, stream, ybuf,
-                   topk_w, T, k, H, out);
+                   topk_w, T, k, H, out, 1);
     else
         MOE_LAUNCH(K_COMBINE, stream, (combine_rows_kernel<uint16_t, MOE_MAX_K>), dim3(blocks), dim3(256), 0, stream,
-                   ybuf, topk_w, T, k, H, out);
+                   ybuf, topk_w, T, k, H, out, 1);
     return hipGetLastError();
 }
 
