@@ -181,31 +181,48 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
     if (blockIdx.x == 0) {
         __shared__ int s_cnt[2][4];
         __shared__ int s_last[4];
+        __shared__ uint8_t s_fm[MOE_MAX_SLOTS];
         const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
         const int nb = np / MM_BM;
+        // format tags into LDS, and each round's block slots (blocks b - 1,
+        // b, b + 1; clamped indices, no branches) loaded one round ahead, so
+        // the rounds wait for no memory round trip of their own
+        for (int i = threadIdx.x; i < n_slots; i += 256) s_fm[i] = fmt[i];
+        const int last = max(nb - 1, 0);
+        int sp = -1, sc = -1, sn = -1;
+        auto load3 = [&](int b0) __attribute__((always_inline)) {
+            const int b = b0 + (int)threadIdx.x;
+            sp = block_slot[min(max(b - 1, 0), last)];
+            sc = block_slot[min(b, last)];
+            sn = block_slot[min(b + 1, last)];
+        };
+        if (nb > 0) load3(0);
+        __syncthreads();
+        // (the round barriers wait for LDS only: the next round's loads stay in flight)
         int base = 0, obase = 0, carry = 0;     // carry: last segment start before this chunk
         for (int b0 = 0; b0 < nb; b0 += 256) {
             const int b = b0 + threadIdx.x;
             const bool valid = b < nb;
-            const int slot = valid ? block_slot[b] : -1;
-            const bool start = valid && (b == 0 || block_slot[b - 1] != slot);
+            const int slot = valid ? sc : -1, prev = sp, next = sn;
+            if (b0 + 256 < nb) load3(b0 + 256);
+            const bool start = valid && (b == 0 || prev != slot);
             const uint64_t smask = __ballot(start);
             const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
             if (lane == 0) s_last[wv] = smask ? b0 + 64 * wv + 63 - __clzll(smask) : -1;
-            __syncthreads();
+            barrier_lds();
             int seg = carry;
             for (int w = 0; w < wv; ++w) seg = s_last[w] > seg ? s_last[w] : seg;
             if (smask & upto) seg = b0 + 64 * wv + 63 - __clzll(smask & upto);
-            const bool f = valid && usable_slot(slot, n_slots, fmt_ok, fmt) >= 0 && fmt[slot] == 0;
+            const bool f = valid && usable_slot(slot, n_slots, fmt_ok, s_fm) >= 0 && s_fm[slot] == 0;
             const bool t = f && ((b - seg) & 1) == 0;
             const bool o = valid && !f;
-            const int nblk = (t && b + 1 < nb && block_slot[b + 1] == slot) ? 2 : 1;
+            const int nblk = (t && b + 1 < nb && next == slot) ? 2 : 1;
             const uint64_t tbal = __ballot(t), obal = __ballot(o);
             if (lane == 0) {
                 s_cnt[0][wv] = __popcll(tbal);
                 s_cnt[1][wv] = __popcll(obal);
             }
-            __syncthreads();
+            barrier_lds();
             int off = base, ooff = obase;
             for (int w = 0; w < wv; ++w) {
                 off += s_cnt[0][w];
@@ -216,7 +233,7 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
             base += s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
             obase += s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
             for (int w = 0; w < 4; ++w) carry = s_last[w] > carry ? s_last[w] : carry;
-            __syncthreads();
+            barrier_lds();
         }
         if (threadIdx.x == 0) {
             *n_tiles = base;
