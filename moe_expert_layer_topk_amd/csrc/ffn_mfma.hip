@@ -69,6 +69,23 @@ constexpr int MM_MAXDESC = 512;                         // held in LDS (later ti
 constexpr int MM_SMEM = MM_DESC + 16 * MM_MAXDESC;
 constexpr int MM_TOK = 1024;                            // KIND 0: token ids of the tile, in its metadata slot
 
+// LDS layout and wave shape per tile kind: a two-block tile is 256 A rows x
+// 256 B rows, 8 waves as 4 (rows) x 2 (columns), 8 B fragments per wave; a
+// one-block tile is 128 A rows x 256 B rows, 8 waves as 2 x 4, 4 B fragments
+template <bool ONE>
+struct MLay {
+    static constexpr int TM = ONE ? MM_BM : MM_TM;          // A rows of a tile
+    static constexpr int OPS = (TM + 256) * 128;            // A rows, 256 B rows of 128 bytes
+    static constexpr int SCL = OPS;                         // 256 row-scale bytes
+    static constexpr int STAGE = OPS + 256;
+    static constexpr int AMAX = MM_RING * STAGE + MM_NMETA * MM_META;
+    static constexpr int DESC = AMAX + 2048;                // row maxima [column waves][A rows] first
+    static constexpr int SMEM = DESC + 16 * MM_MAXDESC;
+    static constexpr int NF = ONE ? 4 : 8;                  // B fragments per wave
+    static constexpr int NA = ONE ? 2 : 4;                  // A row loads (8 rows each) per wave and step
+};
+static_assert(MLay<false>::SMEM == MM_SMEM && MLay<true>::SMEM <= MM_SMEM, "LDS layout");
+
 template <int V>
 struct IC {
     static constexpr int value = V;
@@ -101,7 +118,7 @@ __device__ __forceinline__ void wait_vm() {
     case n: wait_vm<n>(); break;
 __device__ __forceinline__ void wait_vm_n(int n) {
     switch (n) {
-        MM_W(0) MM_W(8) MM_W(9) MM_W(10)
+        MM_W(0) MM_W(6) MM_W(7) MM_W(8) MM_W(9) MM_W(10)
         default: wait_vm<0>(); break;
     }
 }
@@ -163,8 +180,9 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // ------------------------------------------------------------------ prep
 // Block 0 lists, in order, the FP8 tiles (pairs of consecutive blocks of one
 // resident FP8 expert, counted from the start of the expert's segment; an odd
-// last block makes a one-block tile) and the other blocks (int4 or not
-// resident); the other workgroups write, per sorted position, the token, the
+// last block makes a one-block tile; all tiles in one list for the down
+// kernel, the two kinds in lists of their own for the gate/up kernel) and the
+// other blocks (int4 or not resident); the other workgroups write, per sorted position, the token, the
 // route weight and the token's activation scale bytes transposed to
 // [block][K step][row].
 __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restrict__ sorted_pair,
@@ -174,12 +192,14 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
                                                        const float* __restrict__ topk_w,
                                                        const uint8_t* __restrict__ xs, int groups,
                                                        int4* __restrict__ tiles, int* __restrict__ n_tiles,
+                                                       int4* __restrict__ tiles1, int* __restrict__ n_tiles1,
+                                                       int4* __restrict__ tiles2, int* __restrict__ n_tiles2,
                                                        int* __restrict__ others, int* __restrict__ n_others,
                                                        int32_t* __restrict__ tokrow, float* __restrict__ wsort,
                                                        uint8_t* __restrict__ scl) {
     const int np = *n_padded;
     if (blockIdx.x == 0) {
-        __shared__ int s_cnt[2][4];
+        __shared__ int s_cnt[4][4];
         __shared__ int s_last[4];
         __shared__ uint8_t s_fm[MOE_MAX_SLOTS];
         const int lane = lane_id(), wv = threadIdx.x / MOE_WAVE;
@@ -199,7 +219,7 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
         if (nb > 0) load3(0);
         __syncthreads();
         // (the round barriers wait for LDS only: the next round's loads stay in flight)
-        int base = 0, obase = 0, carry = 0;     // carry: last segment start before this chunk
+        int base = 0, base1 = 0, base2 = 0, obase = 0, carry = 0;   // carry: last segment start before this chunk
         for (int b0 = 0; b0 < nb; b0 += 256) {
             const int b = b0 + threadIdx.x;
             const bool valid = b < nb;
@@ -216,28 +236,38 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
             const bool f = valid && usable_slot(slot, n_slots, fmt_ok, s_fm) >= 0 && s_fm[slot] == 0;
             const bool t = f && ((b - seg) & 1) == 0;
             const bool o = valid && !f;
-            const int nblk = (t && b + 1 < nb && next == slot) ? 2 : 1;
-            const uint64_t tbal = __ballot(t), obal = __ballot(o);
+            const bool t2 = t && b + 1 < nb && next == slot, t1 = t && !t2;   // two-block and one-block tiles
+            const uint64_t tbal = __ballot(t), t1bal = __ballot(t1), t2bal = __ballot(t2), obal = __ballot(o);
             if (lane == 0) {
                 s_cnt[0][wv] = __popcll(tbal);
                 s_cnt[1][wv] = __popcll(obal);
+                s_cnt[2][wv] = __popcll(t1bal);
+                s_cnt[3][wv] = __popcll(t2bal);
             }
             barrier_lds();
-            int off = base, ooff = obase;
+            int off = base, ooff = obase, off1 = base1, off2 = base2;
             for (int w = 0; w < wv; ++w) {
                 off += s_cnt[0][w];
                 ooff += s_cnt[1][w];
+                off1 += s_cnt[2][w];
+                off2 += s_cnt[3][w];
             }
-            if (t) tiles[off + __popcll(tbal & lanemask_lt())] = make_int4(b, slot, nblk, 0);
+            if (t) tiles[off + __popcll(tbal & lanemask_lt())] = make_int4(b, slot, t2 ? 2 : 1, 0);
+            if (t1) tiles1[off1 + __popcll(t1bal & lanemask_lt())] = make_int4(b, slot, 1, 0);
+            if (t2) tiles2[off2 + __popcll(t2bal & lanemask_lt())] = make_int4(b, slot, 2, 0);
             if (o) others[ooff + __popcll(obal & lanemask_lt())] = b;
             base += s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
             obase += s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
+            base1 += s_cnt[2][0] + s_cnt[2][1] + s_cnt[2][2] + s_cnt[2][3];
+            base2 += s_cnt[3][0] + s_cnt[3][1] + s_cnt[3][2] + s_cnt[3][3];
             for (int w = 0; w < 4; ++w) carry = s_last[w] > carry ? s_last[w] : carry;
             barrier_lds();
         }
         if (threadIdx.x == 0) {
             *n_tiles = base;
             *n_others = obase;
+            *n_tiles1 = base1;
+            *n_tiles2 = base2;
         }
         return;
     }
@@ -258,20 +288,21 @@ __global__ void __launch_bounds__(256) mfma_prep_kernel(const int32_t* __restric
 // blocks; in a one-block tile the second half repeats the first block's rows
 // and its results are dropped) by 256 B rows (KIND 0: 128 gate + the matching
 // 128 up rows of W13 = 128 columns of h; KIND 1: 256 rows of W2).
-template <int KIND>
-__global__ void __launch_bounds__(MM_THREADS, 1)
-    mfma_ffn_kernel(MPool pool, MTiles tl, const uint8_t* __restrict__ xq, int NP, int H, int I_arg,
-                    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ ybuf) {
+template <int KIND, bool ONE>
+__device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, const uint8_t* __restrict__ xq,
+                                           int NP, int H, int I_arg, uint8_t* __restrict__ hq,
+                                           uint8_t* __restrict__ hs, uint16_t* __restrict__ ybuf, uint8_t* smem) {
+    using Lay = MLay<ONE>;
     const int I = I_arg;
-    extern __shared__ __align__(16) uint8_t smem[];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
     const int m = lane & 15, q = lane >> 4;
-    // 64-row group and 128-column half. Waves w and w + 4 share a SIMD, so
-    // every SIMD holds one wave of each 128-row half of the tile: when a tile
-    // has one block, the waves of its empty half skip their work and every
-    // SIMD does half the matrix work.
-    const int mw = 2 * (wv >> 2) + ((wv >> 1) & 1), nw = wv & 1;
+    // 64-row group and column group. Two-block tiles: 4 x 2; waves w and
+    // w + 4 share a SIMD, so every SIMD holds one wave of each 128-row half
+    // of the tile (the waves of an empty half skip their matrix work). One-
+    // block tiles: 2 x 4, 64 B rows per wave.
+    const int mw = ONE ? (wv >> 2) : 2 * (wv >> 2) + ((wv >> 1) & 1), nw = ONE ? (wv & 3) : (wv & 1);
+    constexpr int NF = Lay::NF, NA = Lay::NA;
     const int S = KIND == 0 ? H / 128 : I / 128;          // K steps per tile
     const int NT = KIND == 0 ? I / 128 : H / 256;         // column tiles per block pair
     const int hgroups = I / 128;
@@ -290,7 +321,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     // trip for all) and the token ids of tile 0 into its metadata slot; later
     // tiles' token ids arrive with the previous tile's first stage
     // (the down kernel keeps scalar loads: the table measured slower there)
-    int4* s_desc = (int4*)(smem + MM_DESC);
+    int4* s_desc = (int4*)(smem + Lay::DESC);
     if (KIND == 0) {
         for (int i = threadIdx.x; i < min(nj, MM_MAXDESC); i += MM_THREADS)
             s_desc[i] = tl.tiles[(start + idx + per_x * i) / NT];
@@ -306,8 +337,8 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     };
     if (KIND == 0) {
         const int4 d0 = desc_of(0);
-        int32_t* s_tok = (int32_t*)(smem + MM_RING * MM_STAGE + MM_TOK);
-        if (threadIdx.x < MM_TM) {
+        int32_t* s_tok = (int32_t*)(smem + MM_RING * Lay::STAGE + MM_TOK);
+        if (threadIdx.x < Lay::TM) {
             const int r = threadIdx.x;
             s_tok[r] = tl.tokrow[(d0.x + (r >= MM_BM && d0.z == 2 ? 1 : 0)) * MM_BM + r % MM_BM];
         }
@@ -344,23 +375,27 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         asm volatile("" : "+v"(lane));
         const int csw0 = 16 * ((lane & 7) ^ ((lane >> 4) & 1));        // loads j even
         const int csw1 = 16 * ((lane & 7) ^ (4 | ((lane >> 4) & 1)));  // loads j odd
-        const int brow0 = KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 + 2 * (wv & 1) + 4 * (lane >> 3)
-                                    : (wv >> 2) * 128 + 2 * (wv & 3) + 8 * (lane >> 3);
+        // one-block tiles: fragment f = 4 nw + n, row m holds output column
+        //   KIND 0: nw * 32 + (n / 2) * I + 2 m + n % 2;  KIND 1: nw * 64 + 4 m + n
+        const int brow0 = ONE ? (KIND == 0 ? (wv & 1) * I + (wv >> 1) * 32 + 2 * (lane >> 3)
+                                           : (wv >> 1) * 64 + 2 * (wv & 1) + 4 * (lane >> 3))
+                              : (KIND == 0 ? ((wv & 3) >> 1) * I + (wv >> 2) * 64 + 2 * (wv & 1) + 4 * (lane >> 3)
+                                           : (wv >> 2) * 128 + 2 * (wv & 3) + 8 * (lane >> 3));
         const int L = start + idx + per_x * j;
         const int4 d = desc_of(j);
         const int b = d.x, nt = L % NT, two = d.z == 2;
         two_next = two;
         const uint8_t* sb = pool.base + (size_t)d.y * pool.stride;
-        const int blk_w = b + ((wv >> 2) & two);            // block of this wave's A rows
-        const int r_w = 32 * (wv & 3);                      // first of them inside the block
+        const int blk_w = ONE ? b : b + ((wv >> 2) & two);  // block of this wave's A rows
+        const int r_w = ONE ? 16 * wv : 32 * (wv & 3);      // first of them inside the block
         bS = tl.scl + (size_t)b * S * MM_BM;
         oS = ((lane >> 5) & two) * S * MM_BM + 4 * (lane & 31);
         if (KIND == 0) {
             // token ids of this wave's 32 rows, from the tile's metadata slot
-            const int32_t* s_tok = (const int32_t*)(smem + MM_RING * MM_STAGE + (j % MM_NMETA) * MM_META + MM_TOK) +
-                                   ((wv >> 2) & 1) * MM_BM + r_w + (lane >> 3);
+            const int32_t* s_tok = (const int32_t*)(smem + MM_RING * Lay::STAGE + (j % MM_NMETA) * MM_META + MM_TOK) +
+                                   (ONE ? 0 : ((wv >> 2) & 1) * MM_BM) + r_w + (lane >> 3);
 #pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2) oA[j2] = (uint32_t)s_tok[8 * j2] * H + ((j2 & 1) ? csw1 : csw0);
+            for (int j2 = 0; j2 < NA; ++j2) oA[j2] = (uint32_t)s_tok[8 * j2] * H + ((j2 & 1) ? csw1 : csw0);
             // waves 4..7: source of 64 token ids of the next tile (loaded with this tile's first stage)
             const int4 dn = desc_of(min(j + 1, nj - 1));
             const int i4 = (wv - 4) & 3;
@@ -388,69 +423,70 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     };
     // vector memory operations stage s puts in flight for this wave
     auto stage_ops = [&](int s) __attribute__((always_inline)) {
-        return 8 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n + (KIND == 0 && wv >= 4 ? 1 : 0) : 0);
+        return NA + 4 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n + (KIND == 0 && wv >= 4 ? 1 : 0) : 0);
     };
     // the loads of step s into LDS buffer u (u = s % 2, except past the end of
     // the stream, where the last step is loaded again into the buffer the
     // current step left, so the loop needs no branch around them)
     auto dma_a = [&](int s, int u, int j2) __attribute__((always_inline)) {
-        uint8_t* st = smem + u * MM_STAGE;
+        uint8_t* st = smem + u * Lay::STAGE;
         const int k0 = (s % S) * 128;
-        dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (32 * wv + 8 * j2) * 128);
+        dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (8 * NA * wv + 8 * j2) * 128);
     };
     auto dma_b = [&](int s, int u, int j2) __attribute__((always_inline)) {
-        uint8_t* st = smem + u * MM_STAGE;
+        uint8_t* st = smem + u * Lay::STAGE;
         const int k0 = (s % S) * 128;
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
-        dma16(bB + ((KIND == 0 ? 32 : 64) * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0),
-              st + MM_TM * 128 + (32 * wv + 8 * j2) * 128);
+        constexpr int RJ = ONE ? (KIND == 0 ? 16 : 32) : (KIND == 0 ? 32 : 64);   // B rows between loads j and j + 1
+        dma16(bB + (RJ * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0),
+              st + Lay::TM * 128 + (32 * wv + 8 * j2) * 128);
     };
     auto dma_tail = [&](int s, int u) __attribute__((always_inline)) {
-        uint8_t* st = smem + u * MM_STAGE;
+        uint8_t* st = smem + u * Lay::STAGE;
         const int g = s % S;
         // opaque copies: the 64-bit addresses are formed here, not kept live
         uint32_t os = oS, om = oM;
         asm volatile("" : "+v"(os));
         asm volatile("" : "+v"(om));
-        if (wv == 0) dma4(bS + g * MM_BM + os, st + MM_SCL);
+        if (wv == 0) dma4(bS + g * MM_BM + os, st + Lay::SCL);
         if (g == 0) {
-            uint8_t* md = smem + MM_RING * MM_STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
+            uint8_t* md = smem + MM_RING * Lay::STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
             for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + om, md + 256 * h);
             if (KIND == 0 && wv >= 4)
-                dma4((const uint8_t*)bT + om, smem + MM_RING * MM_STAGE + ((s / S + 1) % MM_NMETA) * MM_META + MM_TOK +
+                dma4((const uint8_t*)bT + om, smem + MM_RING * Lay::STAGE + ((s / S + 1) % MM_NMETA) * MM_META + MM_TOK +
                                                   256 * (wv - 4));
         }
     };
     auto issue = [&](int s, int u) __attribute__((always_inline)) {
         if (s % S == 0) setup(s / S);
 #pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) dma_a(s, u, j2);
+        for (int j2 = 0; j2 < NA; ++j2) dma_a(s, u, j2);
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2) dma_b(s, u, j2);
         dma_tail(s, u);
     };
 
     // ---- compute side
-    f32x4 acc[4][8];
+    f32x4 acc[4][NF];
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
+            for (int n = 0; n < NF; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
     const int fm = (m >> 1) & 5;
     const int o0 = ((2 * q) ^ fm) << 4, o1 = ((2 * q + 1) ^ fm) << 4;
     // one K step: every fragment of the step is read into registers first, so
     // the LDS buffer can be refilled while the matrix instructions run
-    i32x8 FA[4], FB[8];
+    i32x8 FA[4], FB[NF];
     int SA[4];
     auto read_step = [&](const uint8_t* st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) FB[n] = frag_read(st + MM_TM * 128, 16 * (8 * nw + n) + m, o0, o1);
+        for (int n = 0; n < NF; ++n) FB[n] = frag_read(st + Lay::TM * 128, 16 * (NF * nw + n) + m, o0, o1);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             FA[a] = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
-            SA[a] = st[MM_SCL + 64 * mw + 16 * a + m];
+            SA[a] = st[Lay::SCL + 64 * mw + 16 * a + m];
         }
     };
     // the matrix instructions of one K step with the 16-byte loads of step s
@@ -463,14 +499,19 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
+            for (int n = 0; n < NF; ++n) {
                 // (a wave of an empty tile half issues the loads only; one
                 // sequence with the test at each instruction keeps the
                 // register allocation of a single path)
-                if (live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
-                const int k = 8 * a + n;
-                if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
-                if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+                if (ONE || live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+                const int k = NF * a + n;
+                if (ONE) {
+                    if (k == 1 || k == 3) dma_a(s, u, k >> 1);
+                    if (k >= 5 && k <= 11 && (k & 1)) dma_b(s, u, (k - 5) >> 1);
+                } else {
+                    if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
+                    if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
     };
@@ -484,18 +525,26 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         asm volatile("" : "+s"(I));
         asm volatile("" : "+v"(ln));
         const int m = ln & 15, q = ln >> 4;
-        const uint8_t* md = smem + MM_RING * MM_STAGE + (j % MM_NMETA) * MM_META;
+        const uint8_t* md = smem + MM_RING * Lay::STAGE + (j % MM_NMETA) * MM_META;
         if (KIND == 0) {
-            float* s_amax = (float*)(smem + MM_AMAX);
-            const f32x4 sg = *(const f32x4*)(md + 4 * (nw * 64 + 4 * m));
-            const f32x4 su = *(const f32x4*)(md + 512 + 4 * (nw * 64 + 4 * m));
+            // HN adjacent h columns per lane: fragments n < HN are gate rows,
+            // n + HN the matching up rows; NW column waves share a row
+            constexpr int HN = NF / 2, NW = ONE ? 4 : 2;
+            const int cb = nw * (16 * HN) + HN * m;          // this lane's first h column in the tile
+            float* s_amax = (float*)(smem + Lay::AMAX);
+            float sg[HN], su[HN];
+#pragma unroll
+            for (int n = 0; n < HN; ++n) {
+                sg[n] = *(const float*)(md + 4 * (cb + n));
+                su[n] = *(const float*)(md + 512 + 4 * (cb + n));
+            }
             // with z = g sg (g, u: gate and up accumulators, sg, su: row
             // scales), h = silu(z) (u su) = (g u) (sg su) / (1 + 2^(g (-sg log2 e))):
             // two column constants, so an element costs four multiplies, an
             // add, one exp2 and one reciprocal
-            f32x4 ce, ch;
+            float ce[HN], ch[HN];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
+            for (int n = 0; n < HN; ++n) {
                 ce[n] = sg[n] * -1.44269504088896341f;
                 ch[n] = sg[n] * su[n];
             }
@@ -506,29 +555,35 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                 for (int i = 0; i < 4; ++i) {
                     float mx = 0.f;
 #pragma unroll
-                    for (int n = 0; n < 4; ++n) {
+                    for (int n = 0; n < HN; ++n) {
                         const float g = acc[a][n][i];
                         const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * ce[n]));
-                        const float h = (g * ch[n]) * acc[a][n + 4][i] * r;
+                        const float h = (g * ch[n]) * acc[a][n + HN][i] * r;
                         acc[a][n][i] = h;
                         mx = fmaxf(mx, fabsf(h));
                     }
                     mx = row16_max_nonneg(mx);
-                    if (m == 0) s_amax[nw * MM_TM + 64 * mw + 16 * a + 4 * q + i] = mx;
+                    if (m == 0) s_amax[nw * Lay::TM + 64 * mw + 16 * a + 4 * q + i] = mx;
                 }
             barrier_lds();
-            const int c = nt * 128 + nw * 64 + 4 * m;
+            const int c = nt * 128 + cb;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 64 * mw + 16 * a + 4 * q + i;
-                    int e = pow2_exponent_448(fmaxf(s_amax[row], s_amax[MM_TM + row]));
+                    float amax = s_amax[row];
+#pragma unroll
+                    for (int w2 = 1; w2 < NW; ++w2) amax = fmaxf(amax, s_amax[w2 * Lay::TM + row]);
+                    int e = pow2_exponent_448(amax);
                     e = e < -127 ? -127 : (e > 127 ? 127 : e);
                     const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
-                    const uint32_t hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
+                    uint32_t hi = 0;
+                    if constexpr (HN == 4) hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
                     if (row < rows) {
-                        *(uint32_t*)(hq + (size_t)(b * MM_BM + row) * I + c) = lo | (hi << 16);
+                        uint8_t* dst = hq + (size_t)(b * MM_BM + row) * I + c;
+                        if constexpr (HN == 4) *(uint32_t*)dst = lo | (hi << 16);
+                        else *(uint16_t*)dst = (uint16_t)(lo & 0xFFFFu);
                         if (nw == 0 && m == 0)
                             hs[((size_t)(b + row / MM_BM) * hgroups + nt) * MM_BM + row % MM_BM] = (uint8_t)(e + 127);
                     }
@@ -536,9 +591,12 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         } else {
             const int32_t* s_pr = (const int32_t*)md;
             const float* s_w = (const float*)(md + 1024);
-            const f32x4 sc0 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 8 * m));
-            const f32x4 sc1 = *(const f32x4*)(md + 2048 + 4 * (nw * 128 + 8 * m + 4));
-            const int c = nt * 256 + nw * 128 + 8 * m;        // 8 adjacent columns: one 16-byte store
+            // NF adjacent columns per lane: one 16-byte (8 columns) or 8-byte store
+            const int cb = nw * (16 * NF) + NF * m;
+            f32x4 sc[NF / 4];
+#pragma unroll
+            for (int h = 0; h < NF / 4; ++h) sc[h] = *(const f32x4*)(md + 2048 + 4 * (cb + 4 * h));
+            const int c = nt * 256 + cb;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -546,16 +604,19 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
                     const int row = 64 * mw + 16 * a + 4 * q + i;
                     const int p = s_pr[row];
                     const float w = s_w[row];
-                    uint32_t v[4];
+                    uint32_t v[NF / 2];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const f32x4 sc = h ? sc1 : sc0;
-                        const float y0 = acc[a][4 * h][i] * sc[0] * w, y1 = acc[a][4 * h + 1][i] * sc[1] * w;
-                        const float y2 = acc[a][4 * h + 2][i] * sc[2] * w, y3 = acc[a][4 * h + 3][i] * sc[3] * w;
+                    for (int h = 0; h < NF / 4; ++h) {
+                        const float y0 = acc[a][4 * h][i] * sc[h][0] * w, y1 = acc[a][4 * h + 1][i] * sc[h][1] * w;
+                        const float y2 = acc[a][4 * h + 2][i] * sc[h][2] * w, y3 = acc[a][4 * h + 3][i] * sc[h][3] * w;
                         v[2 * h] = bf16x2_rne(y0, y1);
                         v[2 * h + 1] = bf16x2_rne(y2, y3);
                     }
-                    if (row < rows && p < NP) *(uint4*)(ybuf + (size_t)p * H + c) = make_uint4(v[0], v[1], v[2], v[3]);
+                    if (row < rows && p < NP) {
+                        uint16_t* dst = ybuf + (size_t)p * H + c;
+                        if constexpr (NF == 8) *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
+                        else *(uint2*)dst = make_uint2(v[0], v[1]);
+                    }
                 }
         }
     };
@@ -575,7 +636,7 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
         if (cs % S == 0 && S >= 2) live = mw < 2 || two_next;
         wait_vm_n(stage_ops(min(cs + 1, N - 1)));       // step cs landed
         barrier_lds();                                  // ... for every wave
-        read_step(smem + (cs % MM_RING) * MM_STAGE);   // (a conditional read costs registers)
+        read_step(smem + (cs % MM_RING) * Lay::STAGE);   // (a conditional read costs registers)
         barrier_lds();                                  // every wave has read step cs
         __builtin_amdgcn_sched_barrier(0);
         const int s2 = min(cs + 2, N - 1);
@@ -589,14 +650,34 @@ __global__ void __launch_bounds__(MM_THREADS, 1)
     wait_vm<0>();      // no load into LDS outlives the workgroup
 }
 
+// The FP8 tiles of one GEMM. SPLIT: every workgroup runs its share of the
+// two-block tiles (tl2), then its share of the one-block tiles on their own
+// layout (tl1), each list split over the XCDs and workgroups on its own.
+// Otherwise all tiles (tl) run on the two-block layout, a one-block tile's
+// empty half idle.
+template <int KIND, bool SPLIT>
+__global__ void __launch_bounds__(MM_THREADS, 1)
+    mfma_ffn_kernel(MPool pool, MTiles tl, MTiles tl2, MTiles tl1, const uint8_t* __restrict__ xq, int NP, int H,
+                    int I, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ ybuf) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    if constexpr (SPLIT) {
+        mfma_tiles<KIND, false>(pool, tl2, xq, NP, H, I, hq, hs, ybuf, smem);
+        __syncthreads();                              // LDS is reused by the one-block tiles
+        mfma_tiles<KIND, true>(pool, tl1, xq, NP, H, I, hq, hs, ybuf, smem);
+    } else {
+        mfma_tiles<KIND, false>(pool, tl, xq, NP, H, I, hq, hs, ybuf, smem);
+    }
+}
+
 // ------------------------------------------------------------------ host side
 bool mfma_path_ok(int H, int I) { return H % 256 == 0 && I % 128 == 0 && H <= 2048 && I <= 2048 && H >= 256; }
 
-// workspace: tiles int4[cap/128], counts (256 B), others int[cap/128], tokrow, wsort, scales
+// workspace: tiles int4[cap/128], counts (256 B), others int[cap/128], tokrow, wsort, scales, one-block
+// and two-block tiles int4[cap/128] each
 size_t mfma_ws_bytes(int H, int cap) {
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
     return up((size_t)(cap / MM_BM) * 16) + 256 + up((size_t)(cap / MM_BM) * 4) + up((size_t)cap * 4) * 2 +
-           up((size_t)cap * (H / 128));
+           up((size_t)cap * (H / 128)) + 2 * up((size_t)(cap / MM_BM) * 16);
 }
 
 void mfma_other_list(void* ws, int H, int cap, const int** list, const int** n_list) {
@@ -626,6 +707,8 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     p += up((size_t)(cap / MM_BM) * 16);
     int* n_tiles = (int*)p;
     int* n_others = n_tiles + 1;
+    int* n_tiles1 = n_tiles + 2;
+    int* n_tiles2 = n_tiles + 3;
     p += 256;
     int* others = (int*)p;
     p += up((size_t)(cap / MM_BM) * 4);
@@ -634,6 +717,8 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     float* wsort = (float*)p;
     p += up((size_t)cap * 4);
     uint8_t* scl = p;
+    int4* tiles1 = (int4*)(p + up((size_t)cap * (H / 128)));
+    int4* tiles2 = tiles1 + up((size_t)(cap / MM_BM) * 16) / 16;
 
     MPool mp;
     mp.base = (const uint8_t*)pa.base;
@@ -641,23 +726,49 @@ hipError_t launch_mfma_ffn(const PoolArgs& pa, const uint8_t* xq, const uint8_t*
     for (int i = 0; i < 4; ++i) mp.off[i] = pa.off[0][i];
     int nwg = device_cus() / 8 * 8;
     if (nwg < 8) nwg = 8;
+    // one-block tiles on their own layout when experts average fewer than
+    // three blocks of pairs (one-block tiles are then a large share: C3
+    // T=4096 80% of the tiles, C4 T=8192 35%); at more (C2: 512 pairs per
+    // expert, 29% of the tiles, a fifth of the rows) the second list's
+    // pipeline start costs what the layout saves
+    const bool split = (long)NP < 384L * pa.n_slots;
     if (phase == 0) {
         MOE_LAUNCH(K_MFMA_PREP, stream, mfma_prep_kernel, dim3(1 + (cap + 255) / 256), dim3(256), 0, stream,
                    sorted_pair, block_slot, pa.fmt, pa.n_slots, pa.fmt_ok, n_padded, NP, k, topk_w, xs, H / 128, tiles,
-                   n_tiles, others, n_others, tokrow, wsort, scl);
+                   n_tiles, tiles1, n_tiles1, tiles2, n_tiles2, others, n_others, tokrow, wsort, scl);
         MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, scl};
-        hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
-        if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM1_FP8, stream, mfma_ffn_kernel<0>, dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream, mp, tl, xq,
-                   NP, H, I, hq, hs, ybuf);
+        MTiles tl2{tiles2, n_tiles2, tokrow, wsort, sorted_pair, scl};
+        MTiles tl1{tiles1, n_tiles1, tokrow, wsort, sorted_pair, scl};
+        if (split) {
+            hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0, true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+            if (e != hipSuccess) return e;
+            MOE_LAUNCH(K_GEMM1_FP8, stream, (mfma_ffn_kernel<0, true>), dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream,
+                       mp, tl, tl2, tl1, xq, NP, H, I, hq, hs, ybuf);
+        } else {
+            hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<0, false>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+            if (e != hipSuccess) return e;
+            MOE_LAUNCH(K_GEMM1_FP8, stream, (mfma_ffn_kernel<0, false>), dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream,
+                       mp, tl, tl2, tl1, xq, NP, H, I, hq, hs, ybuf);
+        }
     } else {
         MTiles tl{tiles, n_tiles, tokrow, wsort, sorted_pair, hs};
-        hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<1>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
-        if (e != hipSuccess) return e;
-        MOE_LAUNCH(K_GEMM2_FP8, stream, mfma_ffn_kernel<1>, dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream, mp, tl, xq,
-                   NP, H, I, hq, hs, ybuf);
+        MTiles tl2{tiles2, n_tiles2, tokrow, wsort, sorted_pair, hs};
+        MTiles tl1{tiles1, n_tiles1, tokrow, wsort, sorted_pair, hs};
+        if (split) {
+            hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<1, true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+            if (e != hipSuccess) return e;
+            MOE_LAUNCH(K_GEMM2_FP8, stream, (mfma_ffn_kernel<1, true>), dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream,
+                       mp, tl, tl2, tl1, xq, NP, H, I, hq, hs, ybuf);
+        } else {
+            hipError_t e = hipFuncSetAttribute((const void*)mfma_ffn_kernel<1, false>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, MM_SMEM);
+            if (e != hipSuccess) return e;
+            MOE_LAUNCH(K_GEMM2_FP8, stream, (mfma_ffn_kernel<1, false>), dim3(nwg), dim3(MM_THREADS), MM_SMEM, stream,
+                       mp, tl, tl2, tl1, xq, NP, H, I, hq, hs, ybuf);
+        }
     }
     return hipGetLastError();
 }
