@@ -33,6 +33,11 @@
 // * 8 waves in a 4 x 2 grid over a 256 x 256 tile, 64 x 128 outputs each:
 //   32 v_mfma_scale_f32_16x16x128_f8f6f4 per wave and K step, with the
 //   power-of-two activation exponents (E8M0) as the instruction's A scales;
+// * a lone block (an expert's odd last block) makes a one-block tile; when
+//   experts average fewer than three blocks such tiles are a large share, and
+//   they run after the two-block tiles on a layout of their own (128 x 256,
+//   8 waves in a 2 x 4 grid, 64 x 64 outputs and 16 matrix instructions per
+//   wave and step) instead of idling half of the two-block layout's waves;
 // * B rows are ordered so that the accumulators a lane holds for one row
 //   across fragments are adjacent output columns: epilogue stores are 4-byte
 //   fp8 runs (gate/up: four h columns from four gate and four up fragments)
