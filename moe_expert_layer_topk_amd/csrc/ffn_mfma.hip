@@ -133,8 +133,15 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 // fence waits for every outstanding global load, direct-to-LDS ones included,
 // which would drain the stages in flight. The wave's own LDS traffic is
 // waited for first; direct-to-LDS data is waited for with wait_vm before it.
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Built from the wait and barrier builtins (the compiler then knows the LDS
+// reads before it have completed and adds no waits of its own for them
+// later) between two compiler-only fences that keep memory accesses on their
+// side.
+static __device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0); vmcnt, expcnt left open
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // lane i writes 16 (4) bytes at lds + 16 i (4 i); lds is wave-uniform
@@ -154,15 +161,6 @@ __device__ __forceinline__ int4 sload4(const int4* p) {
     return make_int4(r[0], r[1], r[2], r[3]);
 }
 
-// 32 codes of stage row r for the lane group q (K bytes [32 q, 32 q + 32)):
-// o0, o1 are the lane's swizzled offsets of chunks 2q and 2q+1 (rows read by
-// a lane all share r % 16 = m)
-__device__ __forceinline__ i32x8 frag_read(const uint8_t* st, int r, int o0, int o1) {
-    const i32x4 lo = *(const i32x4*)(st + r * 128 + o0);
-    const i32x4 hi = *(const i32x4*)(st + r * 128 + o1);
-    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // max over each row of 16 lanes (quad swaps, then row rotations by 4 and 8)
 // of non-negative values, as integers: the bit patterns of non-negative
 // floats order like the floats, and an integer max takes its DPP operand
@@ -176,9 +174,12 @@ __device__ __forceinline__ float row16_max_nonneg(float v) {
     return __int_as_float(x);
 }
 
-// two fp32 -> packed bf16, round to nearest even (hardware conversion)
+// two fp32 -> packed bf16, round to nearest even (one hardware conversion of
+// the pair)
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
 }
 
 
@@ -479,46 +480,87 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
 #pragma unroll
             for (int n = 0; n < NF; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
     };
+    // a fragment gives lane m + 16 q the 32 codes of its row m at K bytes
+    // [32 q, 32 q + 32): chunks 2q and 2q+1, at swizzled offsets o0, o1 (every
+    // row a lane reads shares r % 16 = m)
     const int fm = (m >> 1) & 5;
     const int o0 = ((2 * q) ^ fm) << 4, o1 = ((2 * q + 1) ^ fm) << 4;
-    // one K step: every fragment of the step is read into registers first, so
-    // the LDS buffer can be refilled while the matrix instructions run
+    // fragments of a K step in registers: the step being multiplied, and
+    // during the second half of its matrix instructions the next step, each
+    // fragment read again once its last instruction of the step has issued
     i32x8 FA[4], FB[NF];
     int SA[4];
-    auto read_step = [&](const uint8_t* st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < NF; ++n) FB[n] = frag_read(st + Lay::TM * 128, 16 * (NF * nw + n) + m, o0, o1);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            FA[a] = frag_read(st, 64 * mw + 16 * a + m, o0, o1);
-            SA[a] = st[Lay::SCL + 64 * mw + 16 * a + m];
-        }
+    // reads at LDS offset so of a stage; each forms its address from an
+    // opaque copy of the (wave-uniform) row offset, so no address register
+    // stays live across the matrix instructions between the reads
+    const int lo0 = m * 128 + o0, lo1 = m * 128 + o1;   // this lane's two chunks of fragment row m
+    auto lds_frag = [&](int off) __attribute__((always_inline)) {
+        asm volatile("" : "+s"(off));
+        const i32x4 lo = *(const i32x4*)(smem + off + lo0);
+        const i32x4 hi = *(const i32x4*)(smem + off + lo1);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    // the matrix instructions of one K step with the 16-byte loads of step s
-    // between them: a load instruction waits while the CU's load path is
-    // busy, and the matrix pipe keeps working on the instructions issued
-    // before it
-    auto multiply_issue = [&](int s, int u, bool live) __attribute__((always_inline)) {
+    auto read_fb = [&](int so, int n) __attribute__((always_inline)) {
+        FB[n] = lds_frag(so + (Lay::TM + 16 * (NF * nw + n)) * 128);
+    };
+    auto read_fa = [&](int so, int a) __attribute__((always_inline)) {
+        FA[a] = lds_frag(so + (64 * mw + 16 * a) * 128);
+        int off = so + Lay::SCL + 64 * mw + 16 * a;
+        asm volatile("" : "+s"(off));
+        SA[a] = smem[off + m];
+    };
+    auto read_step = [&](int so) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NF; ++n) read_fb(so, n);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) read_fa(so, a);
+    };
+    // the matrix instructions of one K step. First half (A row groups 0, 1):
+    // the 16-byte loads of step s into buffer u between them (a load
+    // instruction waits while the CU's load path is busy, and the matrix pipe
+    // keeps working on the instructions issued before it). Then every wave
+    // waits for the step after this one to land, and (rd) the second half
+    // (row groups 2, 3, alternating) reads it from buffer nx as fragments
+    // come free: A groups 0, 1 first, B fragment n after (3, n), A groups 2,
+    // 3 at the end.
+    // rd: read the next step
+    auto multiply_issue = [&](bool rd, int s, int u, int nx, bool live) __attribute__((always_inline)) {
         dma_tail(s, u);                                 // branches: kept out of the sequence below
         __builtin_amdgcn_sched_barrier(0);
+        constexpr int NK = 4 * NF, HALF = NK / 2;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int n = 0; n < NF; ++n) {
-                // (a wave of an empty tile half issues the loads only; one
-                // sequence with the test at each instruction keeps the
-                // register allocation of a single path)
-                if (ONE || live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
-                const int k = NF * a + n;
-                if (ONE) {
-                    if (k == 1 || k == 3) dma_a(s, u, k >> 1);
-                    if (k >= 5 && k <= 11 && (k & 1)) dma_b(s, u, (k - 5) >> 1);
-                } else {
-                    if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
-                    if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+        for (int k = 0; k < NK; ++k) {
+            const int a = k < HALF ? k / NF : 2 + ((k - HALF) & 1);
+            const int n = k < HALF ? k % NF : (k - HALF) >> 1;
+            if (k == HALF) {
+                wait_vm_n(stage_ops(s));                // the next step landed
+                barrier_lds();                          // ... for every wave
+                if (rd) {
+                    read_fa(nx, 0);
+                    read_fa(nx, 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // (a wave of an empty tile half issues the loads and reads only;
+            // one sequence with the test at each instruction keeps the
+            // register allocation of a single path)
+            if (ONE || live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+            if (ONE) {
+                if (k == 1 || k == 3) dma_a(s, u, k >> 1);
+                if (k >= 4 && k < 8) dma_b(s, u, k - 4);
+            } else {
+                if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
+                if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+            }
+            if (rd) {
+                if (k >= HALF && a == 3) read_fb(nx, n);
+                if (k == NK - 1) {
+                    read_fa(nx, 2);
+                    read_fa(nx, 3);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     auto epilogue = [&](int j) __attribute__((always_inline)) {
         const int L = start + idx + per_x * j;
@@ -545,7 +587,7 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
             }
             // with z = g sg (g, u: gate and up accumulators, sg, su: row
             // scales), h = silu(z) (u su) = (g u) (sg su) / (1 + 2^(g (-sg log2 e))):
-            // two column constants, so an element costs four multiplies, an
+            // two column constants, so an element costs three multiplies, an
             // add, one exp2 and one reciprocal
             float ce[HN], ch[HN];
 #pragma unroll
@@ -553,46 +595,64 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
                 ce[n] = sg[n] * -1.44269504088896341f;
                 ch[n] = sg[n] * su[n];
             }
-            // h replaces the gate accumulators
+            // h replaces the gate accumulators; the 16 row maxima of a lane
+            // are reduced and stored after all of them are formed (one
+            // straight-line block: independent chains interleave)
+            float mx[4][4];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float mx = 0.f;
+                    mx[a][i] = 0.f;
 #pragma unroll
                     for (int n = 0; n < HN; ++n) {
                         const float g = acc[a][n][i];
                         const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * ce[n]));
-                        const float h = (g * ch[n]) * acc[a][n + HN][i] * r;
+                        const float h = (g * acc[a][n + HN][i]) * (ch[n] * r);
                         acc[a][n][i] = h;
-                        mx = fmaxf(mx, fabsf(h));
+                        mx[a][i] = fmaxf(mx[a][i], fabsf(h));
                     }
-                    mx = row16_max_nonneg(mx);
-                    if (m == 0) s_amax[nw * Lay::TM + 64 * mw + 16 * a + 4 * q + i] = mx;
                 }
-            barrier_lds();
-            const int c = nt * 128 + cb;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 64 * mw + 16 * a + 4 * q + i;
-                    float amax = s_amax[row];
+                for (int i = 0; i < 4; ++i) mx[a][i] = row16_max_nonneg(mx[a][i]);
+            if (m == 0) {
 #pragma unroll
-                    for (int w2 = 1; w2 < NW; ++w2) amax = fmaxf(amax, s_amax[w2 * Lay::TM + row]);
-                    int e = pow2_exponent_448(amax);
-                    e = e < -127 ? -127 : (e > 127 ? 127 : e);
-                    const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
-                    uint32_t hi = 0;
-                    if constexpr (HN == 4) hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
-                    if (row < rows) {
-                        uint8_t* dst = hq + (size_t)(b * MM_BM + row) * I + c;
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s_amax[nw * Lay::TM + 64 * mw + 16 * a + 4 * q + i] = mx[a][i];
+            }
+            barrier_lds();
+            // this wave's 64 rows all hold results or all fall in the empty
+            // half of a one-block tile (a wave-uniform test). Stores: a
+            // wave-uniform row base plus a 32-bit lane offset; the four scale
+            // bytes of rows 4q .. 4q+3 (adjacent in hs) in one dword
+            if (64 * mw < rows) {
+                uint8_t* hrow = hq + ((size_t)b * MM_BM + 64 * mw) * I + nt * 128;
+                uint8_t* hsrow = hs + ((size_t)(b + (mw >> 1)) * hgroups + nt) * MM_BM + 64 * (mw & 1);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    uint32_t eb = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 64 * mw + 16 * a + 4 * q + i;
+                        float amax = s_amax[row];
+#pragma unroll
+                        for (int w2 = 1; w2 < NW; ++w2) amax = fmaxf(amax, s_amax[w2 * Lay::TM + row]);
+                        int e = pow2_exponent_448(amax);
+                        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+                        eb |= (uint32_t)(e + 127) << (8 * i);
+                        const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
+                        uint32_t hi = 0;
+                        if constexpr (HN == 4) hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
+                        uint8_t* dst = hrow + (uint32_t)((16 * a + 4 * q + i) * I + cb);
                         if constexpr (HN == 4) *(uint32_t*)dst = lo | (hi << 16);
                         else *(uint16_t*)dst = (uint16_t)(lo & 0xFFFFu);
-                        if (nw == 0 && m == 0)
-                            hs[((size_t)(b + row / MM_BM) * hgroups + nt) * MM_BM + row % MM_BM] = (uint8_t)(e + 127);
                     }
+                    if (nw == 0 && m == 0) *(uint32_t*)(hsrow + 16 * a + 4 * q) = eb;
                 }
+            }
         } else {
             const int32_t* s_pr = (const int32_t*)md;
             const float* s_w = (const float*)(md + 1024);
@@ -601,55 +661,63 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
             f32x4 sc[NF / 4];
 #pragma unroll
             for (int h = 0; h < NF / 4; ++h) sc[h] = *(const f32x4*)(md + 2048 + 4 * (cb + 4 * h));
-            const int c = nt * 256 + cb;
+            // (a wave-uniform test for the empty half of a one-block tile, as
+            // in the gate/up kernel; padding rows per lane)
+            if (64 * mw < rows) {
+                uint16_t* ycol = ybuf + nt * 256 + cb;
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+                for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 64 * mw + 16 * a + 4 * q + i;
-                    const int p = s_pr[row];
-                    const float w = s_w[row];
-                    uint32_t v[NF / 2];
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 64 * mw + 16 * a + 4 * q + i;
+                        const int p = s_pr[row];
+                        const float w = s_w[row];
+                        uint32_t v[NF / 2];
 #pragma unroll
-                    for (int h = 0; h < NF / 4; ++h) {
-                        const float y0 = acc[a][4 * h][i] * sc[h][0] * w, y1 = acc[a][4 * h + 1][i] * sc[h][1] * w;
-                        const float y2 = acc[a][4 * h + 2][i] * sc[h][2] * w, y3 = acc[a][4 * h + 3][i] * sc[h][3] * w;
-                        v[2 * h] = bf16x2_rne(y0, y1);
-                        v[2 * h + 1] = bf16x2_rne(y2, y3);
+                        for (int h = 0; h < NF / 4; ++h) {
+                            const float y0 = acc[a][4 * h][i] * sc[h][0] * w, y1 = acc[a][4 * h + 1][i] * sc[h][1] * w;
+                            const float y2 = acc[a][4 * h + 2][i] * sc[h][2] * w, y3 = acc[a][4 * h + 3][i] * sc[h][3] * w;
+                            v[2 * h] = bf16x2_rne(y0, y1);
+                            v[2 * h + 1] = bf16x2_rne(y2, y3);
+                        }
+                        if (p < NP) {
+                            uint16_t* dst = ycol + (size_t)p * H;
+                            if constexpr (NF == 8) *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
+                            else *(uint2*)dst = make_uint2(v[0], v[1]);
+                        }
                     }
-                    if (row < rows && p < NP) {
-                        uint16_t* dst = ybuf + (size_t)p * H + c;
-                        if constexpr (NF == 8) *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
-                        else *(uint2*)dst = make_uint2(v[0], v[1]);
-                    }
-                }
+            }
         }
     };
 
-    // ---- the stream of K steps. Step s sits in LDS buffer s % 2. Step cs is
-    // read into registers, then (once every wave has read it) its buffer is
-    // refilled with step cs+2, the loads issued between the matrix
-    // instructions of step cs: steps cs+1 and cs+2 are in flight during the
-    // matrix work and the epilogue.
+    // ---- the stream of K steps. Step s sits in LDS buffer s % 2. Step cs
+    // is in registers when its iteration begins; once every wave has read it
+    // its buffer is refilled with step cs+2 during the first half of step
+    // cs's matrix instructions, and step cs+1 is read during the second half
+    // (at a tile's last step: after the epilogue, whose registers it would
+    // otherwise need), so LDS reads, loads and matrix work overlap.
     zero_acc();
     issue(0, 0);
     issue(min(1, N - 1), 1);
+    wait_vm_n(stage_ops(min(1, N - 1)));                // step 0 landed
+    barrier_lds();                                      // ... for every wave
+    read_step(0);
     bool live = true;
     for (int cs = 0; cs < N; ++cs) {
         // with two or more steps per tile, tile cs / S was the last one set
         // up when its first step begins
         if (cs % S == 0 && S >= 2) live = mw < 2 || two_next;
-        wait_vm_n(stage_ops(min(cs + 1, N - 1)));       // step cs landed
-        barrier_lds();                                  // ... for every wave
-        read_step(smem + (cs % MM_RING) * Lay::STAGE);   // (a conditional read costs registers)
         barrier_lds();                                  // every wave has read step cs
         __builtin_amdgcn_sched_barrier(0);
         const int s2 = min(cs + 2, N - 1);
         if (cs + 2 < N && s2 % S == 0) setup(s2 / S);
-        multiply_issue(s2, cs % MM_RING, live);
-        if (cs % S == S - 1) {
+        const int u = cs % MM_RING, nx = ((cs + 1) % MM_RING) * Lay::STAGE;
+        const bool end = cs % S == S - 1;
+        multiply_issue(!end, s2, u, nx, live);
+        if (end) {
             epilogue(cs / S);
             zero_acc();
+            read_step(nx);                              // (past the last step: unused, no branch)
         }
     }
     wait_vm<0>();      // no load into LDS outlives the workgroup
