@@ -174,6 +174,8 @@ __device__ __forceinline__ float row16_max_nonneg(float v) {
     return __int_as_float(x);
 }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
 // two fp32 -> packed bf16, round to nearest even (one hardware conversion of
 // the pair)
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
@@ -586,14 +588,16 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
                 su[n] = *(const float*)(md + 512 + 4 * (cb + n));
             }
             // with z = g sg (g, u: gate and up accumulators, sg, su: row
-            // scales), h = silu(z) (u su) = (g u) (sg su) / (1 + 2^(g (-sg log2 e))):
-            // two column constants, so an element costs three multiplies, an
-            // add, one exp2 and one reciprocal
-            float ce[HN], ch[HN];
+            // scales), h = silu(z) (u su) = (g u) (sg su) / (1 + 2^(g (-sg log2 e)))
+            //   = (g u) / (x c + c),  x = 2^(g ce),  ce = -sg log2 e,  c = 1 / (sg su):
+            // two column constants, so an element costs three multiplies, a
+            // fused multiply-add, one exp2 and one reciprocal (c is held finite:
+            // a zero row scale gives h = 0 as the direct form does)
+            float ce[HN], ic[HN];
 #pragma unroll
             for (int n = 0; n < HN; ++n) {
                 ce[n] = sg[n] * -1.44269504088896341f;
-                ch[n] = sg[n] * su[n];
+                ic[n] = fminf(__builtin_amdgcn_rcpf(sg[n] * su[n]), 3.0e38f);
             }
             // h replaces the gate accumulators; the 16 row maxima of a lane
             // are reduced and stored after all of them are formed (one
@@ -607,8 +611,8 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
 #pragma unroll
                     for (int n = 0; n < HN; ++n) {
                         const float g = acc[a][n][i];
-                        const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * ce[n]));
-                        const float h = (g * acc[a][n + HN][i]) * (ch[n] * r);
+                        const float x = __builtin_amdgcn_exp2f(g * ce[n]);
+                        const float h = (g * acc[a][n + HN][i]) * __builtin_amdgcn_rcpf(fmaf(x, ic[n], ic[n]));
                         acc[a][n][i] = h;
                         mx[a][i] = fmaxf(mx[a][i], fabsf(h));
                     }
@@ -643,12 +647,17 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
                         int e = pow2_exponent_448(amax);
                         e = e < -127 ? -127 : (e > 127 ? 127 : e);
                         eb |= (uint32_t)(e + 127) << (8 * i);
-                        const uint32_t lo = f32x2_to_e4m3(ldexpf(acc[a][0][i], -e), ldexpf(acc[a][1][i], -e));
-                        uint32_t hi = 0;
-                        if constexpr (HN == 4) hi = f32x2_to_e4m3(ldexpf(acc[a][2][i], -e), ldexpf(acc[a][3][i], -e));
+                        // e4m3 codes of h / 2^e: the scaled conversion divides by
+                        // its scale operand (the same codes as converting
+                        // ldexp(h, -e), measured bit-exact over e in [-127, 20])
+                        const float sc = ldexpf(1.0f, e);
+                        const s16x2 z = {0, 0};
+                        const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, acc[a][0][i], acc[a][1][i], sc, false);
                         uint8_t* dst = hrow + (uint32_t)((16 * a + 4 * q + i) * I + cb);
-                        if constexpr (HN == 4) *(uint32_t*)dst = lo | (hi << 16);
-                        else *(uint16_t*)dst = (uint16_t)(lo & 0xFFFFu);
+                        if constexpr (HN == 4)
+                            *(uint32_t*)dst = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                                                                               lo, acc[a][2][i], acc[a][3][i], sc, true));
+                        else *(uint16_t*)dst = (uint16_t)(__builtin_bit_cast(uint32_t, lo) & 0xFFFFu);
                     }
                     if (nw == 0 && m == 0) *(uint32_t*)(hsrow + 16 * a + 4 * q) = eb;
                 }
