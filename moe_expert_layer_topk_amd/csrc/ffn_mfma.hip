@@ -90,6 +90,7 @@ struct MLay {
     static constexpr int NA = ONE ? 2 : 4;                  // A row loads (8 rows each) per wave and step
 };
 static_assert(MLay<false>::SMEM == MM_SMEM && MLay<true>::SMEM <= MM_SMEM, "LDS layout");
+static_assert(MM_RING == 2 && (MM_NMETA & (MM_NMETA - 1)) == 0, "ring and metadata slots index with masks");
 
 template <int V>
 struct IC {
@@ -429,49 +430,52 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
             oM = 4 * lane;
         }
     };
-    // vector memory operations stage s puts in flight for this wave
-    auto stage_ops = [&](int s) __attribute__((always_inline)) {
-        return NA + 4 + (wv == 0 ? 1 : 0) + (s % S == 0 ? meta_n + (KIND == 0 && wv >= 4 ? 1 : 0) : 0);
+    // A step s of the stream is K step g = s % S of tile jt = s / S; the
+    // helpers below take (g, jt), which the loop carries as counters (no
+    // division per step).
+    // vector memory operations stage g puts in flight for this wave
+    auto stage_ops = [&](int g) __attribute__((always_inline)) {
+        return NA + 4 + (wv == 0 ? 1 : 0) + (g == 0 ? meta_n + (KIND == 0 && wv >= 4 ? 1 : 0) : 0);
     };
-    // the loads of step s into LDS buffer u (u = s % 2, except past the end of
+    // the loads of a step into LDS buffer u (u = s % 2, except past the end of
     // the stream, where the last step is loaded again into the buffer the
     // current step left, so the loop needs no branch around them)
-    auto dma_a = [&](int s, int u, int j2) __attribute__((always_inline)) {
+    auto dma_a = [&](int g, int u, int j2) __attribute__((always_inline)) {
         uint8_t* st = smem + u * Lay::STAGE;
-        const int k0 = (s % S) * 128;
+        const int k0 = g * 128;
         dma16(bA + (KIND == 0 ? oA[j2] : oA[j2 & 1] + (size_t)8 * j2 * I) + k0, st + (8 * NA * wv + 8 * j2) * 128);
     };
-    auto dma_b = [&](int s, int u, int j2) __attribute__((always_inline)) {
+    auto dma_b = [&](int g, int u, int j2) __attribute__((always_inline)) {
         uint8_t* st = smem + u * Lay::STAGE;
-        const int k0 = (s % S) * 128;
+        const int k0 = g * 128;
         const size_t KB = KIND == 0 ? (size_t)H : (size_t)I;     // B row length
         constexpr int RJ = ONE ? (KIND == 0 ? 16 : 32) : (KIND == 0 ? 32 : 64);   // B rows between loads j and j + 1
         dma16(bB + (RJ * (j2 & 1) + (j2 >> 1)) * KB + k0 + ((j2 & 1) ? oB1 : oB0),
               st + Lay::TM * 128 + (32 * wv + 8 * j2) * 128);
     };
-    auto dma_tail = [&](int s, int u) __attribute__((always_inline)) {
+    auto dma_tail = [&](int g, int jt, int u) __attribute__((always_inline)) {
         uint8_t* st = smem + u * Lay::STAGE;
-        const int g = s % S;
         // opaque copies: the 64-bit addresses are formed here, not kept live
         uint32_t os = oS, om = oM;
         asm volatile("" : "+v"(os));
         asm volatile("" : "+v"(om));
         if (wv == 0) dma4(bS + g * MM_BM + os, st + Lay::SCL);
         if (g == 0) {
-            uint8_t* md = smem + MM_RING * Lay::STAGE + ((s / S) % MM_NMETA) * MM_META + meta_off;
+            uint8_t* md = smem + MM_RING * Lay::STAGE + (jt & (MM_NMETA - 1)) * MM_META + meta_off;
             for (int h = 0; h < meta_n; ++h) dma4(bM + 256 * h + om, md + 256 * h);
             if (KIND == 0 && wv >= 4)
-                dma4((const uint8_t*)bT + om, smem + MM_RING * Lay::STAGE + ((s / S + 1) % MM_NMETA) * MM_META + MM_TOK +
+                dma4((const uint8_t*)bT + om, smem + MM_RING * Lay::STAGE + ((jt + 1) & (MM_NMETA - 1)) * MM_META + MM_TOK +
                                                   256 * (wv - 4));
         }
     };
     auto issue = [&](int s, int u) __attribute__((always_inline)) {
-        if (s % S == 0) setup(s / S);
+        const int g = s % S, jt = s / S;
+        if (g == 0) setup(jt);
 #pragma unroll
-        for (int j2 = 0; j2 < NA; ++j2) dma_a(s, u, j2);
+        for (int j2 = 0; j2 < NA; ++j2) dma_a(g, u, j2);
 #pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) dma_b(s, u, j2);
-        dma_tail(s, u);
+        for (int j2 = 0; j2 < 4; ++j2) dma_b(g, u, j2);
+        dma_tail(g, jt, u);
     };
 
     // ---- compute side
@@ -526,8 +530,8 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
     // come free: A groups 0, 1 first, B fragment n after (3, n), A groups 2,
     // 3 at the end.
     // rd: read the next step
-    auto multiply_issue = [&](bool rd, int s, int u, int nx, bool live) __attribute__((always_inline)) {
-        dma_tail(s, u);                                 // branches: kept out of the sequence below
+    auto multiply_issue = [&](bool rd, int g, int jt, int u, int nx, bool live) __attribute__((always_inline)) {
+        dma_tail(g, jt, u);                             // branches: kept out of the sequence below
         __builtin_amdgcn_sched_barrier(0);
         constexpr int NK = 4 * NF, HALF = NK / 2;
 #pragma unroll
@@ -535,7 +539,7 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
             const int a = k < HALF ? k / NF : 2 + ((k - HALF) & 1);
             const int n = k < HALF ? k % NF : (k - HALF) >> 1;
             if (k == HALF) {
-                wait_vm_n(stage_ops(s));                // the next step landed
+                wait_vm_n(stage_ops(g));                // the next step landed
                 barrier_lds();                          // ... for every wave
                 if (rd) {
                     read_fa(nx, 0);
@@ -548,11 +552,11 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
             // register allocation of a single path)
             if (ONE || live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
             if (ONE) {
-                if (k == 1 || k == 3) dma_a(s, u, k >> 1);
-                if (k >= 4 && k < 8) dma_b(s, u, k - 4);
+                if (k == 1 || k == 3) dma_a(g, u, k >> 1);
+                if (k >= 4 && k < 8) dma_b(g, u, k - 4);
             } else {
-                if (k < 16 && (k & 3) == 1) dma_a(s, u, k >> 2);
-                if (k < 16 && (k & 3) == 3) dma_b(s, u, k >> 2);
+                if (k < 16 && (k & 3) == 1) dma_a(g, u, k >> 2);
+                if (k < 16 && (k & 3) == 3) dma_b(g, u, k >> 2);
             }
             if (rd) {
                 if (k >= HALF && a == 3) read_fb(nx, n);
@@ -708,25 +712,39 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
     zero_acc();
     issue(0, 0);
     issue(min(1, N - 1), 1);
-    wait_vm_n(stage_ops(min(1, N - 1)));                // step 0 landed
+    wait_vm_n(stage_ops(min(1, N - 1) % S));            // step 0 landed
     barrier_lds();                                      // ... for every wave
     read_step(0);
     bool live = true;
+    // counters: gc = cs % S, jc = cs / S; s2 = min(cs + 2, N - 1) is K step
+    // g2 of tile j2
+    int gc = 0, jc = 0, s2 = min(2, N - 1);
+    int g2 = s2 % S, j2 = s2 / S;
     for (int cs = 0; cs < N; ++cs) {
-        // with two or more steps per tile, tile cs / S was the last one set
-        // up when its first step begins
-        if (cs % S == 0 && S >= 2) live = mw < 2 || two_next;
+        // with two or more steps per tile, tile jc was the last one set up
+        // when its first step begins
+        if (gc == 0 && S >= 2) live = mw < 2 || two_next;
         barrier_lds();                                  // every wave has read step cs
         __builtin_amdgcn_sched_barrier(0);
-        const int s2 = min(cs + 2, N - 1);
-        if (cs + 2 < N && s2 % S == 0) setup(s2 / S);
-        const int u = cs % MM_RING, nx = ((cs + 1) % MM_RING) * Lay::STAGE;
-        const bool end = cs % S == S - 1;
-        multiply_issue(!end, s2, u, nx, live);
+        if (cs + 2 < N && g2 == 0) setup(j2);
+        const int u = cs & 1, nx = ((cs + 1) & 1) * Lay::STAGE;
+        const bool end = gc == S - 1;
+        multiply_issue(!end, g2, j2, u, nx, live);
         if (end) {
-            epilogue(cs / S);
+            epilogue(jc);
             zero_acc();
             read_step(nx);                              // (past the last step: unused, no branch)
+        }
+        if (++gc == S) {
+            gc = 0;
+            ++jc;
+        }
+        if (s2 < N - 1) {
+            ++s2;
+            if (++g2 == S) {
+                g2 = 0;
+                ++j2;
+            }
         }
     }
     wait_vm<0>();      // no load into LDS outlives the workgroup
