@@ -16,13 +16,14 @@
 //   XCDs) take consecutive tiles, so the same token rows and the same
 //   expert's weights are shared in that XCD's L2;
 // * the K steps of all tiles of a workgroup form one stream through two LDS
-//   buffers filled by direct-to-LDS 16-byte loads: a step is read into
-//   registers, its buffer is refilled two steps ahead by loads issued
-//   between the step's matrix instructions (so the CU's load path and the
-//   matrix pipe work at the same time), and the step is multiplied from
-//   registers while the next two are in flight, also across
-//   tile boundaries, so the next tile's loads hide behind the current tile's
-//   last steps and epilogue;
+//   buffers filled by direct-to-LDS 16-byte loads: while a step is
+//   multiplied from registers, its buffer is refilled two steps ahead by
+//   loads issued between the first half of its matrix instructions, and the
+//   next step is read into registers between the second half, each fragment
+//   as soon as its last instruction of the step has issued (so the load
+//   path, the LDS reads and the matrix pipe work at the same time), also
+//   across tile boundaries, so the next tile's loads hide behind the current
+//   tile's last steps and epilogue;
 // * a stage holds 128 A rows and 256 B rows of 128 bytes; one 16-byte load
 //   instruction fills 8 whole rows (full 128-byte lines from memory), each
 //   row's 16-byte chunks XOR-swizzled through the source address of each
