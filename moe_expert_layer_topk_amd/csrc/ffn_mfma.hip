@@ -523,14 +523,13 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
         for (int a = 0; a < 4; ++a) read_fa(so, a);
     };
     // the matrix instructions of one K step. First half (A row groups 0, 1):
-    // the 16-byte loads of step s into buffer u between them (a load
-    // instruction waits while the CU's load path is busy, and the matrix pipe
-    // keeps working on the instructions issued before it). Then every wave
-    // waits for the step after this one to land, and (rd) the second half
-    // (row groups 2, 3, alternating) reads it from buffer nx as fragments
-    // come free: A groups 0, 1 first, B fragment n after (3, n), A groups 2,
-    // 3 at the end.
-    // rd: read the next step
+    // the 16-byte loads of the step two ahead (K step g of tile jt) into
+    // buffer u between them (a load instruction waits while the CU's load
+    // path is busy, and the matrix pipe keeps working on the instructions
+    // issued before it). Then every wave waits for the step after this one to
+    // land, and (rd) the second half (row groups 2, 3, alternating) reads it
+    // from buffer nx as fragments come free: A groups 0, 1 first, B fragment
+    // n after (3, n), A groups 2, 3 at the end.
     auto multiply_issue = [&](bool rd, int g, int jt, int u, int nx, bool live) __attribute__((always_inline)) {
         dma_tail(g, jt, u);                             // branches: kept out of the sequence below
         __builtin_amdgcn_sched_barrier(0);
