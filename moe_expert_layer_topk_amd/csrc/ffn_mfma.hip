@@ -534,6 +534,8 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
         dma_tail(g, jt, u);                             // branches: kept out of the sequence below
         __builtin_amdgcn_sched_barrier(0);
         constexpr int NK = 4 * NF, HALF = NK / 2;
+        constexpr int GRP = KIND == 0 ? 2 : 4;          // matrix instructions per test (measured)
+        static_assert(HALF % GRP == 0, "groups stay inside a half");
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
             const int a = k < HALF ? k / NF : 2 + ((k - HALF) & 1);
@@ -548,9 +550,18 @@ __device__ __forceinline__ void mfma_tiles(const MPool& pool, const MTiles& tl, 
                 __builtin_amdgcn_sched_barrier(0);
             }
             // (a wave of an empty tile half issues the loads and reads only;
-            // one sequence with the test at each instruction keeps the
-            // register allocation of a single path)
-            if (ONE || live) acc[a][n] = mfma_fp8_16x16x128(FA[a], FB[n], acc[a][n], SA[a], 127);
+            // one sequence with the test at each group of GRP instructions
+            // keeps the register allocation of a single path; the loads and
+            // reads placed at an instruction follow its group)
+            if (k % GRP == 0 && (ONE || live)) {
+#pragma unroll
+                for (int d = 0; d < GRP; ++d) {
+                    const int kd = k + d;
+                    const int ad = kd < HALF ? kd / NF : 2 + ((kd - HALF) & 1);
+                    const int nd = kd < HALF ? kd % NF : (kd - HALF) >> 1;
+                    acc[ad][nd] = mfma_fp8_16x16x128(FA[ad], FB[nd], acc[ad][nd], SA[ad], 127);
+                }
+            }
             if (ONE) {
                 if (k == 1 || k == 3) dma_a(g, u, k >> 1);
                 if (k >= 4 && k < 8) dma_b(g, u, k - 4);
